@@ -1,0 +1,319 @@
+"""Benchmark: one KV-cached MAR decode step of the cache-aware path at the MAR-L shape.
+
+A "step" is one non-refresh decoding step of a MAR-L-like model (64 images x 2
+CFG = 128 sequences, 16 heads x 64, N = 320 tokens, active 48 = 16 generating
++ 16 previous + 16 refreshing, 32 layers) through every row of the hot path:
+
+  * the host step plan (refresh decision, budget-filled K);
+  * layer 2: refresh scores + top-K + active/cached partition (mar_refresh_topk);
+  * layers 3..32 (30 layers): cache-aware attention (mar_cache_attn_fwd) and the
+    K/V scatter of the active rows into that layer's cache (mar_kv_scatter_refresh);
+  * the CFG condition cache reuse on the 16-channel token outputs (mar_cfg_residual);
+  * one cosine-gate evaluation on the 1024-wide hidden features (mar_cos_gate).
+
+Every layer owns distinct Q/K/V and cache buffers (about 6.5 GB in all), so the
+256 MB Infinity Cache cannot serve one layer's data to the next.  Inputs are
+seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line.  `value` = active-query tokens per second through the
+cache-aware layers (128 x 48 x 30 per step / step time).  `roofline` describes
+the dominant kernel (the cache-aware attention) with its duration measured by
+HIP events around each of its launches inside the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "cache-aware attn active-query tok/s + HBM GB/s (% peak), MAR-L-like shape"
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mar_l_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "cache_aware_attention_amd", "csrc", "cache_attn.hip")
+
+
+def attn_bytes(B, H, A, Nc, D, elem=2):
+    """Algorithmic bytes of one cache-aware attention call: read Q_A, K_A, V_A,
+    write out (4 x A rows), read the Nc cached K and V rows, read the cached
+    index list once per sequence."""
+    return B * H * (4 * A + 2 * Nc) * D * elem + B * Nc * 4
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(calls_bytes):
+    """Counter-measured HBM bytes per attention launch, if taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_hash(ATTN_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, plan_nc, cfg, args):
+    """The oracle on a bounded sample of the step: one full layer-call of the
+    attention (all 2048 (b,h) units), one layer's scatter, the top-K, the CFG
+    residual and the gate, then the step time = fixed parts + 30 x per-layer parts."""
+    import numpy as np
+    import torch
+
+    import oracle
+    nt = oracle.num_threads()
+    t64 = lambda t: t.detach().double().cpu().numpy()
+    b16 = lambda t: t.detach().view(torch.int16).cpu().numpy()
+    L = x["layers"][0]
+    q, ka, va = t64(L["q_a"]), t64(L["k_a"]), t64(L["v_a"])
+    kc, vc = t64(L["k_cache"]), t64(L["v_cache"])
+    cidx = x["cached_idx"].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.cache_attention(q, ka, va, kc, vc, cidx, cfg.D ** -0.5, Nc=plan_nc)
+    t_attn = time.perf_counter() - t0
+    del q, ka, va, kc, vc
+    kcb, vcb, kab, vab = (b16(L[k]) for k in ("k_cache", "v_cache", "k_a", "v_a"))
+    act = x["active_idx"].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.kv_scatter(kcb, vcb, kab, vab, act)
+    t_scatter = time.perf_counter() - t0
+    qg, kf = t64(x["q_gen"]), t64(x["k_full"])
+    gp = x["gp"].cpu().numpy()
+    t0 = time.perf_counter()
+    s = oracle.refresh_scores(qg, kf, cfg.D ** -0.5)
+    oracle.refresh_select(s, gp, cfg.K)
+    t_topk = time.perf_counter() - t0
+    del qg, kf
+    c, r = x["cond"].cpu().numpy(), x["residual"].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.cfg_residual(c, residual=r, mode=1)
+    t_cfg = time.perf_counter() - t0
+    xg, yg = t64(x["gate_x"]), t64(x["gate_y"])
+    t0 = time.perf_counter()
+    oracle.cos_gate(xg, yg, float(np.float32(0.95)))
+    t_gate = time.perf_counter() - t0
+    n_ca = cfg.layers - 2
+    t_step = t_topk + t_cfg + t_gate + n_ca * (t_attn + t_scatter)
+    tokens = cfg.B * cfg.A * n_ca
+    return {
+        "value": tokens / t_step, "unit": "tok/s", "cores": nt, "kind": "oracle",
+        "sample": (f"one MAR-L layer-call of attention (2048 units) and of the scatter, plus "
+                   f"top-K, CFG residual and gate once; step time = fixed + {n_ca} x per-layer "
+                   f"(measured {t_attn + t_scatter + t_topk + t_cfg + t_gate:.1f} s of CPU work)"),
+        "seconds": {"attn_layer": t_attn, "scatter_layer": t_scatter, "topk": t_topk,
+                    "cfg": t_cfg, "gate": t_gate, "step_extrapolated": t_step},
+    }
+
+
+def build_inputs(cfg, dev):
+    import numpy as np
+    import torch
+
+    from mar_workloads import (attention_inputs, cfg_outputs, device_gate_features,
+                               device_normal, generation_order)
+    import cache_aware_attention_amd as marca
+
+    n_ca = cfg.layers - 2
+    layers = []
+    for l in range(n_ca):
+        x = attention_inputs(cfg, dev, seed=cfg.seed * 100 + l)
+        x.pop("cfg")
+        x["out"] = torch.empty_like(x["q_a"])
+        layers.append(x)
+        torch.cuda.synchronize()
+    order = torch.from_numpy(generation_order(cfg)).to(dev)
+    # a mid-decode step with 16 previous and 16 generating tokens: P then G is one slice
+    prev_begin = 96
+    gp = order[:, prev_begin:prev_begin + cfg.n_prev + cfg.n_gen]
+    q_gen = device_normal((cfg.B, cfg.H, cfg.n_gen, cfg.D), 71, dev, torch.bfloat16)
+    k_full = device_normal((cfg.B, cfg.H, cfg.N, cfg.D), 72, dev, torch.bfloat16)
+    c0, u0, c1, _ = cfg_outputs(cfg.B_img, cfg.n_img, cfg.cfg_channels, seed=cfg.seed)
+    gx, gy, _ = device_gate_features(cfg.B, cfg.N, cfg.W, seed=cfg.seed, device=dev)
+    x = {
+        "layers": layers, "gp": gp, "q_gen": q_gen, "k_full": k_full,
+        "scores": torch.empty((cfg.B, cfg.N), dtype=torch.float32, device=dev),
+        "active_idx": torch.empty((cfg.B, cfg.A), dtype=torch.int32, device=dev),
+        "cached_idx": torch.empty((cfg.B, cfg.N), dtype=torch.int32, device=dev),
+        "cached_len": torch.empty((cfg.B,), dtype=torch.int32, device=dev),
+        "workspace": torch.empty((marca.mar_refresh_topk_workspace(cfg.B, cfg.H, cfg.N) // 4,),
+                                 dtype=torch.float32, device=dev),
+        "cond": torch.from_numpy(c1).to(dev),
+        "residual": torch.from_numpy(c0 - u0).to(dev),
+        "uncond_out": torch.empty(c1.shape, dtype=torch.float32, device=dev),
+        "gate_x": gx, "gate_y": gy,
+        "cos": torch.empty((cfg.B, cfg.N), dtype=torch.float32, device=dev),
+        "reuse": torch.empty((cfg.B, cfg.N), dtype=torch.uint8, device=dev),
+        "cidx": torch.empty((cfg.B, cfg.N), dtype=torch.int32, device=dev),
+        "clen": torch.empty((cfg.B,), dtype=torch.int32, device=dev),
+    }
+    torch.cuda.synchronize()
+    return x
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run the plain copy kernel (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence with no collective; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import cache_aware_attention_amd as marca
+    from mar_workloads import CONFIGS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS["mar_l"]
+
+    if args.copy_only:
+        # plain copy of a known size through the full-refresh kernel: 2 x 256 MiB read,
+        # 2 x 256 MiB written per launch
+        n = 256 * 1024 * 1024 // 2
+        a = torch.empty(n, dtype=torch.bfloat16, device=dev).view(1, 1, n // 64, 64)
+        b = torch.empty_like(a); c = torch.empty_like(a); d = torch.empty_like(a)
+        for _ in range(5):
+            marca.mar_kv_scatter_refresh(a, b, c, d, None)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": 2 * n * 2,
+                          "copy_bytes_written_per_launch": 2 * n * 2}))
+        return
+
+    print(f"bench: building MAR-L inputs ({cfg.layers - 2} cache-aware layers)", file=sys.stderr,
+          flush=True)
+    x = build_inputs(cfg, dev)
+    counts = [cfg.n_gen] * (cfg.steps)
+    counts[0] = 0
+    step_t = 4  # a non-refresh step (4 % 3 != 0) with 16 previous + 16 generating tokens
+    n_ca = cfg.layers - 2
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def one_step(timers=None):
+        plan = marca.mar_plan_step(counts, step_t, cfg.N, cfg.budget)
+        assert not plan.refresh and plan.n_active == cfg.A and plan.n_cached == cfg.Nc
+        if timers is not None:
+            e0 = ev(); e0.record(stream)
+        marca.mar_refresh_topk(x["q_gen"], x["k_full"], x["gp"], plan.n_prev + plan.n_gen,
+                               plan.n_refresh, scores=x["scores"], active_idx=x["active_idx"],
+                               cached_idx=x["cached_idx"], cached_len=x["cached_len"],
+                               workspace=x["workspace"])
+        if timers is not None:
+            e1 = ev(); e1.record(stream); timers["topk"].append((e0, e1))
+        for l in range(n_ca):
+            L = x["layers"][l]
+            if timers is not None:
+                a0 = ev(); a0.record(stream)
+            marca.mar_cache_attn_fwd(L["q_a"], L["k_a"], L["v_a"], L["k_cache"], L["v_cache"],
+                                     x["cached_idx"], Nc=plan.n_cached, out=L["out"])
+            if timers is not None:
+                a1 = ev(); a1.record(stream); timers["attn"].append((a0, a1))
+            marca.mar_kv_scatter_refresh(L["k_cache"], L["v_cache"], L["k_a"], L["v_a"],
+                                         x["active_idx"])
+            if timers is not None:
+                a2 = ev(); a2.record(stream); timers["scatter"].append((a1, a2))
+        if timers is not None:
+            c0 = ev(); c0.record(stream)
+        marca.mar_cfg_residual(x["cond"], residual=x["residual"], mode=marca.MAR_CFG_REUSE,
+                               uncond_out=x["uncond_out"])
+        if timers is not None:
+            c1 = ev(); c1.record(stream); timers["cfg"].append((c0, c1))
+        marca.mar_cos_gate(x["gate_x"], x["gate_y"], 0.95, cos_out=x["cos"],
+                           reuse_mask=x["reuse"], compute_idx=x["cidx"], compute_len=x["clen"])
+        if timers is not None:
+            c2 = ev(); c2.record(stream); timers["gate"].append((c1, c2))
+
+    print("bench: warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # Timed region 1: whole steps, no per-kernel events.
+    print("bench: timing steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    s0, s1 = ev(), ev()
+    t0 = time.perf_counter()
+    s0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = s0.elapsed_time(s1) / args.steps
+
+    # Timed region 2: the same steps with HIP events around every launch.
+    timers = {k: [] for k in ("topk", "attn", "scatter", "cfg", "gate")}
+    for _ in range(args.steps):
+        one_step(timers)
+    torch.cuda.synchronize()
+    avg_us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in timers.items()}
+
+    tokens_per_step = cfg.B * cfg.A * n_ca
+    value = tokens_per_step / (ms_per_step * 1e-3)
+    bytes_call = attn_bytes(cfg.B, cfg.H, cfg.A, cfg.Nc, cfg.D)
+    achieved = bytes_call / (avg_us["attn"] * 1e-6) / 1e9
+    traffic = load_traffic(bytes_call)
+
+    copy_gbs = None
+    try:  # achievable HBM: the plain full-refresh copy over one layer's caches
+        L0, L1 = x["layers"][0], x["layers"][1]
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(10):
+            marca.mar_kv_scatter_refresh(L0["k_cache"], L0["v_cache"], L1["k_cache"],
+                                         L1["v_cache"], None)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        nbytes = 4 * L0["k_cache"].numel() * 2
+        copy_gbs = nbytes / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    except Exception as exc:  # noqa: BLE001 - reported, not fatal
+        print(f"bench: copy measurement failed: {exc}", file=sys.stderr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: oracle CPU baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(x, cfg.Nc, cfg, args)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal Q/K/V, cache = fresh + noise at cosine ~0.95)",
+        "config": {"workload": "mar_l_decode_step", "sequences": cfg.B, "heads": cfg.H,
+                   "head_dim": cfg.D, "tokens": cfg.N, "active": cfg.A, "cached": cfg.Nc,
+                   "cache_aware_layers": n_ca, "refresh_k": cfg.K, "gate_width": cfg.W,
+                   "cfg_residual": [cfg.B_img, cfg.n_img, cfg.cfg_channels]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "kernel_us": avg_us,
+        "attn_bytes_per_call": bytes_call,
+        "attn_tok_per_s": cfg.B * cfg.A / (avg_us["attn"] * 1e-6),
+        "copy_gbs": copy_gbs,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

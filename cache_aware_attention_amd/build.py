@@ -1,0 +1,75 @@
+"""Build libmarca.so in-tree: hipcc for the gfx950 kernels, g++ for the host ABI.
+
+Run as ``python -m cache_aware_attention_amd.build`` or through
+``__graft_entry__.build()``.  Objects go to ``_build/`` next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+BUILD = PKG / "_build"
+LIB = PKG / "libmarca.so"
+
+HIP_SOURCES = ["cache_attn.hip", "kv_scatter.hip", "refresh_topk.hip", "cos_gate.hip",
+               "cfg_residual.hip"]
+CPP_SOURCES = ["abi.cpp", "schedule.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and Path(cand).exists():
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmarca)")
+
+
+def hip_flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+            # no packed fp32 instructions in device code
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # hipcc's host pass warns about the device-only feature flag; drop that noise
+    msg = "\n".join(l for l in r.stderr.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if msg.strip():
+        print(msg, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> Path:
+    BUILD.mkdir(exist_ok=True)
+    jobs = []
+    for src in HIP_SOURCES:
+        obj = BUILD / (src + ".o")
+        jobs.append([hipcc(), *hip_flags(), "-c", str(CSRC / src), "-o", str(obj)])
+    for src in CPP_SOURCES:
+        obj = BUILD / (src + ".o")
+        jobs.append(["g++", "-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra",
+                     f"-I{INCLUDE}", f"-I{CSRC}", "-c", str(CSRC / src), "-o", str(obj)])
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
+        list(ex.map(_run, jobs))
+    objs = [str(BUILD / (s + ".o")) for s in HIP_SOURCES + CPP_SOURCES]
+    tmp = LIB.with_suffix(f".so.tmp{os.getpid()}")
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *objs])
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

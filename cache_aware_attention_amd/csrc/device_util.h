@@ -1,0 +1,77 @@
+// device_util.h -- small device helpers shared by the HIP kernels of libmarca
+// (bf16 conversion, 64-lane wave reductions, prefix scans).  gfx950 only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "mar_cache_attn.h"
+
+namespace marca {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// bfloat16 <-> float.  Widening is exact; narrowing uses gfx950's
+// v_cvt_pk_bf16_f32 (round to nearest even, NaN stays NaN).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Two floats -> packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return static_cast<uint16_t>(pack_bf16x2(f, 0.f) & 0xffffu);
+}
+
+// Butterfly reductions over the 64 lanes of a wave; every lane gets the
+// result and the combination order is fixed, so results are deterministic.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Exclusive prefix sum of one int per thread over a block of kThreads
+// threads (multiple of 64).  `scratch` holds kThreads/64 ints of LDS.
+// Returns the exclusive prefix; *total receives the block sum.
+template <int kThreads>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) scratch[wid] = incl;
+    __syncthreads();
+    int wave_off = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+        int s = scratch[w];
+        if (w < wid) wave_off += s;
+        sum += s;
+    }
+    __syncthreads();
+    *total = sum;
+    return wave_off + incl - v;
+}
+
+inline int status_from_launch() {
+    return hipGetLastError() == hipSuccess ? MAR_OK : MAR_E_LAUNCH;
+}
+
+}  // namespace marca

@@ -1,0 +1,153 @@
+"""Host-side checks of libmarca's C ABI (no GPU needed).
+
+The library must load, export every function include/mar_cache_attn.h
+declares, reject bad arguments with the documented status before any GPU work,
+and its host step planner must agree with the oracle's schedule.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cache_aware_attention_amd import _lib
+from mar_workloads import CONFIGS, cosine_counts
+from oracle import schedule as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mar_cache_attn.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_RANGE, E_WS, E_LAUNCH, E_UNSUP = 0, -1, -2, -3, -4, -5, -6, -7
+P = 0x10000  # a 16-byte aligned stand-in address; never dereferenced (calls fail first)
+BAD = 0x10008  # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mar_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    raw = ctypes.CDLL(str(_lib._LIB_PATH))
+    for n in names:
+        assert hasattr(raw, n), f"{n} not exported"
+
+
+def test_status_strings(lib):
+    for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_RANGE, E_WS, E_LAUNCH, E_UNSUP):
+        s = lib.mar_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.mar_status_string(-99).decode() == "unknown status"
+    assert lib.mar_version() >= 100
+
+
+def attn(lib, q=P, ka=P, va=P, kc=P, vc=P, cidx=P, ldc=272, out=P, lse=None, B=2, H=2, N=320,
+         A=48, Nc=272, D=64, scale=0.125, dtype=1):
+    return lib.mar_cache_attn_fwd(q, ka, va, kc, vc, cidx, ldc, out, lse, B, H, N, A, Nc, D,
+                                  scale, dtype, None)
+
+
+def test_cache_attn_rejections(lib):
+    assert attn(lib, q=None) == E_NULL
+    assert attn(lib, out=None) == E_NULL
+    assert attn(lib, cidx=None) == E_NULL          # Nc > 0 needs a list
+    assert attn(lib, dtype=7) == E_DTYPE
+    assert attn(lib, A=0) == E_SHAPE
+    assert attn(lib, B=0) == E_SHAPE
+    assert attn(lib, Nc=-1) == E_SHAPE
+    assert attn(lib, A=49) == E_SHAPE              # A + Nc > N
+    assert attn(lib, ldc=100) == E_SHAPE           # ldc < Nc
+    assert attn(lib, D=128) == E_UNSUP
+    assert attn(lib, scale=float("nan")) == E_RANGE
+    assert attn(lib, kc=BAD) == E_RANGE            # misaligned
+
+
+def test_scatter_rejections(lib):
+    f = lib.mar_kv_scatter_refresh
+    assert f(None, P, P, P, P, 48, None, 2, 2, 320, 48, 64, 1, None) == E_NULL
+    assert f(P, P, P, P, P, 48, None, 2, 2, 320, 48, 64, 9, None) == E_DTYPE
+    assert f(P, P, P, P, None, 0, None, 2, 2, 320, 48, 64, 1, None) == E_SHAPE   # full needs M==N
+    assert f(P, P, P, P, P, 10, None, 2, 2, 320, 48, 64, 1, None) == E_SHAPE     # ld_idx < M
+    assert f(P, P, P, P, P, 48, None, 2, 2, 320, 48, 4, 1, None) == E_UNSUP      # 8-byte rows
+    assert f(P, BAD, P, P, P, 48, None, 2, 2, 320, 48, 64, 1, None) == E_RANGE
+
+
+def topk(lib, q=P, k=P, gp=P, ld_gp=256, n_gp=32, K=16, scores=P, act=P, ld_act=48, cac=P,
+         ld_cac=272, clen=P, ws=P, ws_bytes=None, B=2, H=2, G=16, N=320, D=64, dtype=1):
+    if ws_bytes is None:
+        ws_bytes = B * H * N * 4
+    return lib.mar_refresh_topk(q, k, gp, ld_gp, n_gp, K, 0.125, scores, act, ld_act, cac, ld_cac,
+                                clen, ws, ws_bytes, B, H, G, N, D, dtype, None)
+
+
+def test_topk_rejections(lib):
+    assert lib.mar_refresh_topk_workspace(2, 3, 5) == 2 * 3 * 5 * 4
+    assert lib.mar_refresh_topk_workspace(0, 3, 5) == 0
+    assert topk(lib, scores=None) == E_NULL
+    assert topk(lib, gp=None) == E_NULL
+    assert topk(lib, dtype=3) == E_DTYPE
+    assert topk(lib, K=-1) == E_RANGE
+    assert topk(lib, K=300) == E_RANGE             # n_gp + K > N
+    assert topk(lib, G=65) == E_UNSUP
+    assert topk(lib, ld_act=40) == E_SHAPE
+    assert topk(lib, ld_cac=100) == E_SHAPE
+    assert topk(lib, ld_gp=10) == E_SHAPE
+    assert topk(lib, N=5000, ld_cac=5000) == E_UNSUP
+    assert topk(lib, ws=None) == E_WS
+    assert topk(lib, ws_bytes=100) == E_WS
+
+
+def test_gate_and_cfg_rejections(lib):
+    g = lib.mar_cos_gate
+    assert g(None, P, 0.95, 1e-8, P, P, P, P, 2, 10, 64, 1, None) == E_NULL
+    assert g(P, P, 0.95, 1e-8, P, P, P, P, 2, 10, 64, 5, None) == E_DTYPE
+    assert g(P, P, 0.95, 1e-8, P, P, P, P, 2, 0, 64, 1, None) == E_SHAPE
+    assert g(P, P, 0.95, 1e-8, P, P, P, P, 2, 10, 12, 1, None) == E_UNSUP      # 24-byte rows
+    assert g(P, P, float("nan"), 1e-8, P, P, P, P, 2, 10, 64, 1, None) == E_RANGE
+    assert g(P, P, 0.95, -1.0, P, P, P, P, 2, 10, 64, 1, None) == E_RANGE
+    c = lib.mar_cfg_residual
+    assert c(P, P, P, None, None, 1.0, 5, 16, None) == E_RANGE                   # bad mode
+    assert c(P, None, P, None, None, 1.0, 0, 16, None) == E_NULL                 # store needs uncond
+    assert c(P, None, P, None, None, 1.0, 1, 16, None) == E_NULL                 # reuse needs out
+    assert c(P, P, P, None, None, 1.0, 0, -1, None) == E_SHAPE
+    assert c(P, BAD, P, None, None, 1.0, 0, 16, None) == E_RANGE
+
+
+@pytest.mark.parametrize("name", ["mar_b", "mar_l", "mar_h", "highres"])
+def test_plan_step_matches_oracle(lib, name):
+    cfg = CONFIGS[name]
+    counts = cosine_counts(cfg.n_img, cfg.steps)
+    for warmup in (0, 2):
+        for t in range(cfg.steps):
+            ref = S.plan_step(counts, t, cfg.N, cfg.budget, 3, warmup)
+            got = _lib.mar_plan_step(counts, t, cfg.N, cfg.budget, 3, warmup)
+            assert got.refresh == int(ref.refresh)
+            for f in ("step", "gen_begin", "n_gen", "prev_begin", "n_prev", "n_refresh",
+                      "n_active", "n_cached"):
+                assert getattr(got, f) == getattr(ref, f), (t, f)
+            for layer in range(1, cfg.layers + 1):
+                fl = _lib.mar_layer_flags(got, layer)
+                assert bool(fl & _lib.MAR_LAYER_CACHE) == (S.layer_kind(ref, layer) == S.CACHE)
+                assert bool(fl & _lib.MAR_LAYER_SELECT) == S.selects_refresh(ref, layer)
+                assert bool(fl & _lib.MAR_LAYER_GATE) == S.gate_applies(ref, layer)
+
+
+def test_plan_step_rejections(lib):
+    plan = _lib.StepPlan()
+    arr = (ctypes.c_int32 * 3)(1, 2, 3)
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    assert lib.mar_plan_step(None, 3, 0, 10, 4, 3, 0, ctypes.byref(plan)) == E_NULL
+    assert lib.mar_plan_step(p, 3, 3, 10, 4, 3, 0, ctypes.byref(plan)) == E_RANGE
+    assert lib.mar_plan_step(p, 3, 0, 10, 4, 0, 0, ctypes.byref(plan)) == E_SHAPE
+    assert lib.mar_plan_step(p, 3, 2, 5, 4, 3, 0, ctypes.byref(plan)) == E_RANGE  # 6 > 5 tokens
+    assert lib.mar_layer_flags(None, 1, 2, 2, 3) == E_NULL
+    with pytest.raises(_lib.MarError):
+        _lib.mar_plan_step([1, 2], 5, 10, 4)
