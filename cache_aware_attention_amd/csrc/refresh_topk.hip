@@ -9,9 +9,10 @@
 // cached = every other token.
 //
 // Kernel 1 (one workgroup per (sequence, head)): two passes over the head's
-// keys per group of up to 16 queries -- pass 1 builds each query's softmax
-// max and normaliser with the running (max, sum) rule, pass 2 sums the
-// normalised probabilities over the queries into a per-(b,h,token) partial.
+// keys -- pass 1 builds each query's softmax max and normaliser with the
+// running (max, sum) rule, pass 2 sums the normalised probabilities over the
+// queries into a per-(b,h,token) partial.  bf16 runs the score tiles on MFMA;
+// fp32 uses a plain FMA version.
 // Kernel 2 (one workgroup per sequence): sums the partials over heads in a
 // fixed order (no float atomics, deterministic), ranks the eligible tokens
 // with a bitonic sort of 64-bit keys (orderable score << 32 | ~index, so equal
@@ -24,30 +25,7 @@ namespace marca {
 namespace {
 
 constexpr int kD = 64;
-constexpr int kQG = 16;  // queries per pass group
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ void load_row(const float* p, float (&x)[kD]) {
-#pragma unroll
-    for (int c = 0; c < kD / 4; ++c) {
-        const float4 a = reinterpret_cast<const float4*>(p)[c];
-        x[4 * c] = a.x; x[4 * c + 1] = a.y; x[4 * c + 2] = a.z; x[4 * c + 3] = a.w;
-    }
-}
-__device__ __forceinline__ void load_row(const uint16_t* p, float (&x)[kD]) {
-#pragma unroll
-    for (int c = 0; c < kD / 8; ++c) {
-        const uint4 a = reinterpret_cast<const uint4*>(p)[c];
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
-            x[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-        }
-    }
-}
-__device__ __forceinline__ float load1(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ float load1(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
 
 // Merge two running softmax states (max m, sum l) in base 2.
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
@@ -59,93 +37,181 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2)
     l = a + c;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void refresh_scores_kernel(
-    const T* __restrict__ q_gen, const T* __restrict__ k_full, float* __restrict__ ws, int G,
-    int N, float scale_log2) {
-    __shared__ float q_s[kQG][kD];
-    __shared__ float red_m[kThreads / kWave][kQG], red_l[kThreads / kWave][kQG];
-    __shared__ float stat_m[kQG], stat_inv[kQG];
+// fp32 version of kernel 1: plain FMA, one generating query at a time with
+// block-wide max and sum reductions (three sweeps over the head's keys per
+// query; this path serves float inputs, not the bf16 decoding shapes).
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* scratch) {
+    v = is_max ? wave_max(v) : wave_sum(v);
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    __syncthreads();
+    if (lane == 0) scratch[wid] = v;
+    __syncthreads();
+    float r = scratch[0];
+    for (int w = 1; w < kThreads / kWave; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
+    return r;
+}
+
+__device__ __forceinline__ float dot_row(const float* q_s, const float* k) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < kD / 4; ++c) {
+        const float4 a = reinterpret_cast<const float4*>(k)[c];
+        s = fmaf(q_s[4 * c], a.x, s);
+        s = fmaf(q_s[4 * c + 1], a.y, s);
+        s = fmaf(q_s[4 * c + 2], a.z, s);
+        s = fmaf(q_s[4 * c + 3], a.w, s);
+    }
+    return s;
+}
+
+__global__ __launch_bounds__(kThreads) void refresh_scores_f32_kernel(
+    const float* __restrict__ q_gen, const float* __restrict__ k_full, float* __restrict__ ws,
+    int G, int N, float scale_log2) {
+    __shared__ float q_s[kD];
+    __shared__ float scratch[kThreads / kWave];
     extern __shared__ float acc_s[];  // [N]
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wid = tid / kWave;
     const int u = blockIdx.x;
-    const T* K = k_full + (size_t)u * N * kD;
-
+    const float* K = k_full + (size_t)u * N * kD;
     for (int j = tid; j < N; j += kThreads) acc_s[j] = 0.f;
-
-    for (int g0 = 0; g0 < G; g0 += kQG) {
-        const int ng = min(kQG, G - g0);
+    for (int g = 0; g < G; ++g) {
         __syncthreads();
-        for (int e = tid; e < kQG * kD; e += kThreads) {
-            const int gq = e / kD, d = e % kD;
-            q_s[gq][d] = (gq < ng) ? load1(q_gen, ((size_t)u * G + g0 + gq) * kD + d) * scale_log2
-                                   : 0.f;
-        }
+        if (tid < kD) q_s[tid] = q_gen[((size_t)u * G + g) * kD + tid] * scale_log2;
         __syncthreads();
-
-        // Pass 1: per-query running max / normaliser over this thread's keys.
-        float m[kQG], l[kQG];
-#pragma unroll
-        for (int gq = 0; gq < kQG; ++gq) {
-            m[gq] = -INFINITY;
-            l[gq] = 0.f;
-        }
-        for (int j = tid; j < N; j += kThreads) {
-            float kr[kD];
-            load_row(K + (size_t)j * kD, kr);
-#pragma unroll
-            for (int gq = 0; gq < kQG; ++gq) {
-                if (gq < ng) {
-                    float s = 0.f;
-#pragma unroll
-                    for (int d = 0; d < kD; ++d) s = fmaf(q_s[gq][d], kr[d], s);
-                    merge_ml(m[gq], l[gq], s, 1.f);
-                }
-            }
-        }
-#pragma unroll
-        for (int gq = 0; gq < kQG; ++gq) {
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const float mo = __shfl_xor(m[gq], o, kWave);
-                const float lo = __shfl_xor(l[gq], o, kWave);
-                merge_ml(m[gq], l[gq], mo, lo);
-            }
-            if (lane == 0) {
-                red_m[wid][gq] = m[gq];
-                red_l[wid][gq] = l[gq];
-            }
-        }
-        __syncthreads();
-        if (tid < kQG) {
-            float mm = red_m[0][tid], ll = red_l[0][tid];
-            for (int w = 1; w < kThreads / kWave; ++w) merge_ml(mm, ll, red_m[w][tid], red_l[w][tid]);
-            stat_m[tid] = mm;
-            stat_inv[tid] = (ll > 0.f) ? 1.f / ll : 0.f;
-        }
-        __syncthreads();
-
-        // Pass 2: sum of normalised probabilities over the group's queries.
-        for (int j = tid; j < N; j += kThreads) {
-            float kr[kD];
-            load_row(K + (size_t)j * kD, kr);
-            float a = 0.f;
-#pragma unroll
-            for (int gq = 0; gq < kQG; ++gq) {
-                if (gq < ng) {
-                    float s = 0.f;
-#pragma unroll
-                    for (int d = 0; d < kD; ++d) s = fmaf(q_s[gq][d], kr[d], s);
-                    a += exp2f(s - stat_m[gq]) * stat_inv[gq];
-                }
-            }
-            acc_s[j] += a;
-        }
+        float mloc = -INFINITY;
+        for (int j = tid; j < N; j += kThreads) mloc = fmaxf(mloc, dot_row(q_s, K + (size_t)j * kD));
+        const float M = block_reduce(mloc, true, scratch);
+        float lloc = 0.f;
+        for (int j = tid; j < N; j += kThreads) lloc += exp2f(dot_row(q_s, K + (size_t)j * kD) - M);
+        const float inv = 1.f / block_reduce(lloc, false, scratch);
+        for (int j = tid; j < N; j += kThreads)
+            acc_s[j] += exp2f(dot_row(q_s, K + (size_t)j * kD) - M) * inv;
     }
     __syncthreads();
     for (int j = tid; j < N; j += kThreads) ws[(size_t)u * N + j] = acc_s[j];
+}
+
+// bf16 path of kernel 1 on MFMA.  Workgroup of 4 waves per (sequence, head);
+// S = Q K^T tiles of 16 queries x 16 keys on v_mfma_f32_16x16x32_bf16 (Q as
+// the A operand, 16-byte pieces of key rows as the B operand), so a lane
+// holds S[query 4g+i][key m16].  Pass 1 keeps a running (max, sum) per query
+// over the wave's key tiles, merged across the 16 lanes of a group and then
+// across the waves; pass 2 recomputes S (the head's keys are re-read, mostly
+// from L2), normalises, and sums over the queries in registers and two lane
+// shuffles.  Each key tile belongs to one wave, so no accumulation races.
+template <int QT>
+__global__ __launch_bounds__(kThreads) void refresh_scores_mfma_kernel(
+    const uint16_t* __restrict__ q_gen, const uint16_t* __restrict__ k_full,
+    float* __restrict__ ws, int G, int N, float scale_log2) {
+    constexpr int kWaves = kThreads / kWave;
+    __shared__ float red_m[kWaves][QT * 16], red_l[kWaves][QT * 16];
+    __shared__ float stat_m[QT * 16], stat_inv[QT * 16];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int g = lane >> 4, m16 = lane & 15;
+    const int u = blockIdx.x;
+
+    bf16x8_t qa[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int q = qt * 16 + m16;
+        uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+        if (q < G) {
+            const uint4* p = reinterpret_cast<const uint4*>(q_gen + ((size_t)u * G + q) * kD);
+            lo = p[g];
+            hi = p[4 + g];
+        }
+        qa[qt][0] = __builtin_bit_cast(bf16x8_t, lo);
+        qa[qt][1] = __builtin_bit_cast(bf16x8_t, hi);
+    }
+    const uint16_t* K = k_full + (size_t)u * N * kD;
+    const int ntiles = (N + 15) / 16;
+
+    auto tile_scores = [&](int t, f32x4_t (&s)[QT]) {
+        const int key = 16 * t + m16;
+        const uint4* p = reinterpret_cast<const uint4*>(K + (size_t)(key < N ? key : 0) * kD);
+        const bf16x8_t k0 = __builtin_bit_cast(bf16x8_t, p[g]);
+        const bf16x8_t k1 = __builtin_bit_cast(bf16x8_t, p[4 + g]);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qt][0], k0, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qt][1], k1, acc, 0, 0, 0);
+            s[qt] = acc;
+        }
+    };
+
+    // Pass 1: running max / sum per query over this wave's key tiles.
+    float m[QT][4], l[QT][4];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[qt][i] = -INFINITY;
+            l[qt][i] = 0.f;
+        }
+    for (int t = w; t < ntiles; t += kWaves) {
+        f32x4_t s[QT];
+        tile_scores(t, s);
+        const bool valid = 16 * t + m16 < N;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = valid ? s[qt][i] * scale_log2 : -INFINITY;
+                const float M = fmaxf(m[qt][i], v);
+                const float Mr = (M == -INFINITY) ? 0.f : M;
+                l[qt][i] = l[qt][i] * __builtin_amdgcn_exp2f(m[qt][i] - Mr) +
+                           __builtin_amdgcn_exp2f(v - Mr);
+                m[qt][i] = M;
+            }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1)
+                merge_ml(m[qt][i], l[qt][i], __shfl_xor(m[qt][i], o, kWave),
+                         __shfl_xor(l[qt][i], o, kWave));
+            if (m16 == 0) {
+                red_m[w][qt * 16 + 4 * g + i] = m[qt][i];
+                red_l[w][qt * 16 + 4 * g + i] = l[qt][i];
+            }
+        }
+    __syncthreads();
+    if (tid < QT * 16) {
+        float mm = red_m[0][tid], ll = red_l[0][tid];
+        for (int v = 1; v < kWaves; ++v) merge_ml(mm, ll, red_m[v][tid], red_l[v][tid]);
+        stat_m[tid] = (mm == -INFINITY) ? 0.f : mm;
+        stat_inv[tid] = (tid < G && ll > 0.f) ? 1.f / ll : 0.f;  // padded queries add 0
+    }
+    __syncthreads();
+
+    // Pass 2: normalised probabilities summed over the queries, per key.
+    float sm[QT][4], si[QT][4];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sm[qt][i] = stat_m[qt * 16 + 4 * g + i];
+            si[qt][i] = stat_inv[qt * 16 + 4 * g + i];
+        }
+    for (int t = w; t < ntiles; t += kWaves) {
+        f32x4_t s[QT];
+        tile_scores(t, s);
+        float col = 0.f;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                col += __builtin_amdgcn_exp2f(s[qt][i] * scale_log2 - sm[qt][i]) * si[qt][i];
+        col += __shfl_xor(col, 16, kWave);
+        col += __shfl_xor(col, 32, kWave);
+        const int key = 16 * t + m16;
+        if (g == 0 && key < N) ws[(size_t)u * N + key] = col;
+    }
 }
 
 __device__ __forceinline__ uint64_t rank_key(float s, int j) {
@@ -245,11 +311,16 @@ int launch_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp
     const float scale_log2 = scale * 1.4426950408889634f;
     const size_t lds1 = (size_t)N * sizeof(float);
     if (dtype == MAR_BF16) {
-        hipLaunchKernelGGL(refresh_scores_kernel<uint16_t>, dim3(B * H), dim3(kThreads), lds1,
-                           stream, static_cast<const uint16_t*>(q_gen),
-                           static_cast<const uint16_t*>(k_full), workspace, G, N, scale_log2);
+        const int qt = (G + 15) / 16;
+        const dim3 grid(B * H), block(kThreads);
+        switch (qt) {
+            case 1: hipLaunchKernelGGL(refresh_scores_mfma_kernel<1>, grid, block, 0, stream, static_cast<const uint16_t*>(q_gen), static_cast<const uint16_t*>(k_full), workspace, G, N, scale_log2); break;
+            case 2: hipLaunchKernelGGL(refresh_scores_mfma_kernel<2>, grid, block, 0, stream, static_cast<const uint16_t*>(q_gen), static_cast<const uint16_t*>(k_full), workspace, G, N, scale_log2); break;
+            case 3: hipLaunchKernelGGL(refresh_scores_mfma_kernel<3>, grid, block, 0, stream, static_cast<const uint16_t*>(q_gen), static_cast<const uint16_t*>(k_full), workspace, G, N, scale_log2); break;
+            default: hipLaunchKernelGGL(refresh_scores_mfma_kernel<4>, grid, block, 0, stream, static_cast<const uint16_t*>(q_gen), static_cast<const uint16_t*>(k_full), workspace, G, N, scale_log2); break;
+        }
     } else {
-        hipLaunchKernelGGL(refresh_scores_kernel<float>, dim3(B * H), dim3(kThreads), lds1, stream,
+        hipLaunchKernelGGL(refresh_scores_f32_kernel, dim3(B * H), dim3(kThreads), lds1, stream,
                            static_cast<const float*>(q_gen), static_cast<const float*>(k_full),
                            workspace, G, N, scale_log2);
     }
