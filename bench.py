@@ -17,8 +17,9 @@ seeded synthetic tensors already resident in HBM.
 
 Prints ONE JSON line.  `value` = active-query tokens per second through the
 cache-aware layers (128 x 48 x 30 per step / step time).  `roofline` describes
-the dominant kernel (the cache-aware attention) with its duration measured by
-HIP events around each of its launches inside the timed steps.
+the dominant kernel (the cache-aware attention); its average launch duration is
+measured with HIP events on the launch stream around the 30 back-to-back
+attention launches of each timed step.
 """
 from __future__ import annotations
 
@@ -63,10 +64,11 @@ def load_traffic(calls_bytes):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, plan_nc, cfg, args):
-    """The oracle on a bounded sample of the step: one full layer-call of the
-    attention (all 2048 (b,h) units), one layer's scatter, the top-K, the CFG
-    residual and the gate, then the step time = fixed parts + 30 x per-layer parts."""
+def cpu_baseline(x, plan_nc, cfg, args, budget_s=12.0):
+    """The oracle on a bounded sample of the step: the top-K, the CFG residual and
+    the gate once, then whole layer-calls of the attention (all 2048 (b,h) units)
+    and of the scatter, layer after layer, until about `budget_s` seconds of CPU
+    work are spent; step time = fixed parts + 30 x the mean per-layer time."""
     import numpy as np
     import torch
 
@@ -74,19 +76,7 @@ def cpu_baseline(x, plan_nc, cfg, args):
     nt = oracle.num_threads()
     t64 = lambda t: t.detach().double().cpu().numpy()
     b16 = lambda t: t.detach().view(torch.int16).cpu().numpy()
-    L = x["layers"][0]
-    q, ka, va = t64(L["q_a"]), t64(L["k_a"]), t64(L["v_a"])
-    kc, vc = t64(L["k_cache"]), t64(L["v_cache"])
-    cidx = x["cached_idx"].cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.cache_attention(q, ka, va, kc, vc, cidx, cfg.D ** -0.5, Nc=plan_nc)
-    t_attn = time.perf_counter() - t0
-    del q, ka, va, kc, vc
-    kcb, vcb, kab, vab = (b16(L[k]) for k in ("k_cache", "v_cache", "k_a", "v_a"))
-    act = x["active_idx"].cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.kv_scatter(kcb, vcb, kab, vab, act)
-    t_scatter = time.perf_counter() - t0
+    spent = 0.0
     qg, kf = t64(x["q_gen"]), t64(x["k_full"])
     gp = x["gp"].cpu().numpy()
     t0 = time.perf_counter()
@@ -102,16 +92,35 @@ def cpu_baseline(x, plan_nc, cfg, args):
     t0 = time.perf_counter()
     oracle.cos_gate(xg, yg, float(np.float32(0.95)))
     t_gate = time.perf_counter() - t0
+    spent = t_topk + t_cfg + t_gate
+    cidx = x["cached_idx"].cpu().numpy()
+    act = x["active_idx"].cpu().numpy()
+    t_attn, t_scatter, n_layers = 0.0, 0.0, 0
+    for L in x["layers"]:
+        q, ka, va = t64(L["q_a"]), t64(L["k_a"]), t64(L["v_a"])
+        kc, vc = t64(L["k_cache"]), t64(L["v_cache"])
+        t0 = time.perf_counter()
+        oracle.cache_attention(q, ka, va, kc, vc, cidx, cfg.D ** -0.5, Nc=plan_nc)
+        t_attn += time.perf_counter() - t0
+        del q, ka, va, kc, vc
+        kcb, vcb, kab, vab = (b16(L[k]) for k in ("k_cache", "v_cache", "k_a", "v_a"))
+        t0 = time.perf_counter()
+        oracle.kv_scatter(kcb, vcb, kab, vab, act)
+        t_scatter += time.perf_counter() - t0
+        n_layers += 1
+        if spent + t_attn + t_scatter >= budget_s:
+            break
     n_ca = cfg.layers - 2
-    t_step = t_topk + t_cfg + t_gate + n_ca * (t_attn + t_scatter)
+    per_layer = (t_attn + t_scatter) / n_layers
+    t_step = t_topk + t_cfg + t_gate + n_ca * per_layer
     tokens = cfg.B * cfg.A * n_ca
     return {
         "value": tokens / t_step, "unit": "tok/s", "cores": nt, "kind": "oracle",
-        "sample": (f"one MAR-L layer-call of attention (2048 units) and of the scatter, plus "
-                   f"top-K, CFG residual and gate once; step time = fixed + {n_ca} x per-layer "
-                   f"(measured {t_attn + t_scatter + t_topk + t_cfg + t_gate:.1f} s of CPU work)"),
-        "seconds": {"attn_layer": t_attn, "scatter_layer": t_scatter, "topk": t_topk,
-                    "cfg": t_cfg, "gate": t_gate, "step_extrapolated": t_step},
+        "sample": (f"{n_layers} MAR-L layer-calls of attention (2048 (b,h) units each) and of "
+                   f"the scatter, plus top-K, CFG residual and gate once; step time = fixed + "
+                   f"{n_ca} x mean per-layer ({spent + t_attn + t_scatter:.1f} s of CPU work)"),
+        "seconds": {"attn_per_layer": t_attn / n_layers, "scatter_per_layer": t_scatter / n_layers,
+                    "topk": t_topk, "cfg": t_cfg, "gate": t_gate, "step_extrapolated": t_step},
     }
 
 
@@ -208,39 +217,63 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def one_step(timers=None):
-        plan = marca.mar_plan_step(counts, step_t, cfg.N, cfg.budget)
-        assert not plan.refresh and plan.n_active == cfg.A and plan.n_cached == cfg.Nc
-        if timers is not None:
-            e0 = ev(); e0.record(stream)
+    def topk(plan):
         marca.mar_refresh_topk(x["q_gen"], x["k_full"], x["gp"], plan.n_prev + plan.n_gen,
                                plan.n_refresh, scores=x["scores"], active_idx=x["active_idx"],
                                cached_idx=x["cached_idx"], cached_len=x["cached_len"],
                                workspace=x["workspace"])
-        if timers is not None:
-            e1 = ev(); e1.record(stream); timers["topk"].append((e0, e1))
-        for l in range(n_ca):
-            L = x["layers"][l]
-            if timers is not None:
-                a0 = ev(); a0.record(stream)
-            marca.mar_cache_attn_fwd(L["q_a"], L["k_a"], L["v_a"], L["k_cache"], L["v_cache"],
-                                     x["cached_idx"], Nc=plan.n_cached, out=L["out"])
-            if timers is not None:
-                a1 = ev(); a1.record(stream); timers["attn"].append((a0, a1))
-            marca.mar_kv_scatter_refresh(L["k_cache"], L["v_cache"], L["k_a"], L["v_a"],
-                                         x["active_idx"])
-            if timers is not None:
-                a2 = ev(); a2.record(stream); timers["scatter"].append((a1, a2))
-        if timers is not None:
-            c0 = ev(); c0.record(stream)
+
+    def attn(l, plan):
+        L = x["layers"][l]
+        marca.mar_cache_attn_fwd(L["q_a"], L["k_a"], L["v_a"], L["k_cache"], L["v_cache"],
+                                 x["cached_idx"], Nc=plan.n_cached, out=L["out"])
+
+    def scatter(l):
+        L = x["layers"][l]
+        marca.mar_kv_scatter_refresh(L["k_cache"], L["v_cache"], L["k_a"], L["v_a"],
+                                     x["active_idx"])
+
+    def cfg_reuse():
         marca.mar_cfg_residual(x["cond"], residual=x["residual"], mode=marca.MAR_CFG_REUSE,
                                uncond_out=x["uncond_out"])
-        if timers is not None:
-            c1 = ev(); c1.record(stream); timers["cfg"].append((c0, c1))
+
+    def gate():
         marca.mar_cos_gate(x["gate_x"], x["gate_y"], 0.95, cos_out=x["cos"],
                            reuse_mask=x["reuse"], compute_idx=x["cidx"], compute_len=x["clen"])
-        if timers is not None:
-            c2 = ev(); c2.record(stream); timers["gate"].append((c1, c2))
+
+    def plan_step():
+        plan = marca.mar_plan_step(counts, step_t, cfg.N, cfg.budget)
+        assert not plan.refresh and plan.n_active == cfg.A and plan.n_cached == cfg.Nc
+        return plan
+
+    def one_step():
+        """One decode step in model order: top-K at layer 2, then per cache-aware
+        layer its attention and the scatter of its fresh rows, then CFG + gate."""
+        plan = plan_step()
+        topk(plan)
+        for l in range(n_ca):
+            attn(l, plan)
+            scatter(l)
+        cfg_reuse()
+        gate()
+
+    def timed_kernels():
+        """The same launches as one step, grouped by kernel so that one pair of HIP
+        events brackets each group of back-to-back launches (an event pair around
+        every single launch adds its own overhead to the measured time)."""
+        plan = plan_step()
+        spans = {}
+        def span(name, fn, n):
+            e0 = ev(); e0.record(stream)
+            fn()
+            e1 = ev(); e1.record(stream)
+            spans[name] = (e0, e1, n)
+        span("topk", lambda: topk(plan), 1)
+        span("attn", lambda: [attn(l, plan) for l in range(n_ca)], n_ca)
+        span("scatter", lambda: [scatter(l) for l in range(n_ca)], n_ca)
+        span("cfg", cfg_reuse, 1)
+        span("gate", gate, 1)
+        return spans
 
     print("bench: warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -260,12 +293,11 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = s0.elapsed_time(s1) / args.steps
 
-    # Timed region 2: the same steps with HIP events around every launch.
-    timers = {k: [] for k in ("topk", "attn", "scatter", "cfg", "gate")}
-    for _ in range(args.steps):
-        one_step(timers)
+    # Timed region 2: the same launches, grouped per kernel, HIP events per group.
+    groups = [timed_kernels() for _ in range(args.steps)]
     torch.cuda.synchronize()
-    avg_us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in timers.items()}
+    avg_us = {k: 1e3 * sum(g[k][0].elapsed_time(g[k][1]) for g in groups)
+              / sum(g[k][2] for g in groups) for k in groups[0]}
 
     tokens_per_step = cfg.B * cfg.A * n_ca
     value = tokens_per_step / (ms_per_step * 1e-3)
