@@ -24,6 +24,8 @@
 //
 // Head dim is fixed at 64 (MAR-B/L/H all use 64).  The cached index list is
 // sanitised: an entry outside [0, N) is skipped, never dereferenced.
+#include <type_traits>
+
 #include "device_util.h"
 #include "launch.h"
 
@@ -133,11 +135,43 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(
 
 // ---------------------------------------------------------------------------
 // MFMA path (bf16, A >= 16)
+//
+// One 64-lane wave per (sequence, head) unit and group of up to 16*NQT
+// queries.  The virtual key/value sequence [active rows ; cached rows] is
+// streamed in chunks of 32 rows; one or two further chunks are in flight
+// while one is computed.  Per chunk:
+//  * K goes from HBM straight into MFMA operand registers: lane (g, m16)
+//    loads 16-byte pieces g and 4+g of key row 16t + m16, which is the A
+//    operand layout of S^T = K Q^T on v_mfma_f32_16x16x32_bf16.  Each load
+//    instruction reads 64-byte halves of 16 rows.
+//  * V is loaded as whole 128-byte rows (lane l: row 8k + l/8, piece l%8, so
+//    one instruction reads 8 complete rows), stored to LDS with the 16-byte
+//    piece p of row r at slot p ^ (r & 7), and read back with the transposing
+//    ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T.
+//  * The S^T accumulator layout (lane (g, m16) holds keys 16t + 4g + i of
+//    query m16) is directly the B operand P^T of the PV product, with k-slot
+//    j <-> key row 16(j>>2) + 4g + (j&3); the V^T reads use the same map.
+//  * Online softmax in base 2 with a lazily updated reference max: the state
+//    is rescaled only when a score exceeds the reference by more than
+//    kRescaleLog2 (in log2 units), so probabilities stay <= 2^kRescaleLog2.
+//    Rescaling by 2^(m_old - m_new) folds chunk after chunk -- the active
+//    rows first, the cached rows after -- into one (max, sum, weighted sum)
+//    state, which is the merge rule of the two partial softmax sums.
+//  * The softmax denominator is accumulated by one more MFMA with an all-ones
+//    A operand, so numerator and denominator sum the same bf16 probabilities.
+// Rows past the end of the sequence and cached entries outside [0, N) load
+// active row 0 instead (always valid) and are masked to -inf.  The unit's
+// cached index list is staged in LDS once; chunks made only of active rows
+// are requested before that list arrives.  The output tile goes through LDS
+// so that every store instruction writes whole 128-byte rows.
 // ---------------------------------------------------------------------------
-constexpr int kChunk = 32;         // key rows per iteration (two 16-row MFMA tiles)
-constexpr int kVStride = 80;       // LDS row stride of staged V, in bf16 (160 bytes)
+constexpr int kChunk = 32;          // key rows per chunk (two 16-row MFMA tiles)
 constexpr int kQueriesPerGroup = 64;
 constexpr int kMaxMfmaTokens = 8192;
+constexpr float kRescaleLog2 = 8.f;
+// Chunks in flight ahead of the one computed: two where the registers allow
+// (up to 48 queries per wave), one for 64 queries.
+constexpr int prefetch_depth(int nqt) { return nqt <= 3 ? 2 : 1; }
 
 union U4 {
     uint4 u;
@@ -150,32 +184,53 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) {
     return t.v;
 }
 
-// Element offset of key/value row r of the virtual sequence [active ; cached]
-// from the unit's active base (r < A) or cache base (otherwise), with a flag
-// for "row exists".  Branch-free: invalid rows point at active row 0, which
-// always exists (A >= 1), and are zeroed / masked by the caller.
-struct RowRef {
-    const uint16_t* p;
-    bool ok;
-};
-__device__ __forceinline__ RowRef row_ref(int r, int A, int Nc, const int32_t* cidx_s,
-                                          const uint16_t* base_a, const uint16_t* base_c) {
-    const int c = r - A;
-    const bool in_c = (c >= 0) && (c < Nc);
-    const int n = cidx_s[in_c ? c : 0];  // cidx_s has at least one entry
-    const bool is_a = r < A;
-    const bool ok = is_a || (in_c && n >= 0);
-    const uint16_t* pa = base_a + (size_t)(is_a ? r : 0) * kD;
-    const uint16_t* pc = base_c + (size_t)(n >= 0 ? n : 0) * kD;
-    RowRef ref;
-    ref.p = (!is_a && ok) ? pc : pa;
-    ref.ok = ok;
-    return ref;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Byte offset of logical 16-byte piece `piece` of 128-byte row r in a
+// swizzled LDS tile.
+__device__ __forceinline__ int swz(int r, int piece) { return r * 128 + ((piece ^ (r & 7)) << 4); }
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16): within each 16-lane
+// group, lane i receives element (i mod 4) of the 8-byte chunk addressed by
+// lane 4e + i/4 of the group, for e = 0..3.
+__device__ __forceinline__ uint2 lds_tr_b64(const unsigned char* p) {
+    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(p));
+    return __builtin_bit_cast(uint2, v);
 }
 
-__device__ __forceinline__ uint4 zero_unless(bool ok, uint4 x) {
-    return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
+// Maximum over lanes l, l^16, l^32, l^48 (register-only lane swaps).
+__device__ __forceinline__ float max_over_groups(float x) {
+    const uint32_t u = __float_as_uint(x);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(x);
+    auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+
+// Row r of the virtual sequence [active ; cached] of one unit: a pointer to
+// its 64 elements and whether it exists.  Missing rows point at active row 0.
+__device__ __forceinline__ const uint16_t* row_ptr(int r, int A, int Nc, const int32_t* cidx_s,
+                                                   const uint16_t* base_a,
+                                                   const uint16_t* base_c, bool& ok) {
+    const int c = r - A;
+    const bool is_a = r < A;
+    const bool in_c = static_cast<unsigned>(c) < static_cast<unsigned>(Nc);
+    const int n = cidx_s[in_c ? c : 0];  // the list area holds at least one entry
+    ok = is_a || (in_c && n >= 0);
+    const uint16_t* pc = base_c + static_cast<size_t>(n >= 0 ? n : 0) * kD;
+    const uint16_t* pa = base_a + static_cast<size_t>(is_a ? r : 0) * kD;
+    return (!is_a && ok) ? pc : pa;
+}
+
+// Registers of one chunk in flight.
+struct ChunkRegs {
+    uint4 k[2][2];   // K operand pieces: rows 16t + m16, pieces g and 4+g
+    uint4 v[4];      // V rows 8k + lane/8, piece lane%8
+    uint32_t valid;  // bit j: key row j of the chunk exists (wave-uniform)
+};
 
 template <int NQT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
@@ -185,13 +240,16 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
                       const int32_t* __restrict__ cached_idx, int ldc,
                       uint16_t* __restrict__ out, float* __restrict__ lse, int units, int H,
                       int N, int A, int Nc, int n_groups, float scale_log2) {
+    constexpr int kPF = prefetch_depth(NQT);
+    static_assert(kPF >= 1 && kPF <= 3, "prefetch depth");
+    constexpr int kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem);                         // [32][80]
-    int32_t* cidx_s = reinterpret_cast<int32_t*>(smem + kChunk * kVStride * 2); // [Nc]
+    unsigned char* tile = smem;  // V chunk, later the output tile
+    int32_t* cidx_s = reinterpret_cast<int32_t*>(smem + kTileBytes);  // [max(Nc, 1)]
 
     const int lane = threadIdx.x;
-    const int g = lane >> 4;    // lane group: k-slot group of MFMA operands
-    const int m16 = lane & 15;  // row/column within a 16x16 tile
+    const int g = lane >> 4;    // lane group: k-slot group of the MFMA operands
+    const int m16 = lane & 15;  // row / column within a 16x16 tile
 
     // Work mapping.  With several query groups per unit, the groups of one
     // unit are placed on the same XCD (workgroups are dealt round-robin over
@@ -205,200 +263,238 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         const int slot = blockIdx.x >> 3;
         u = (slot / n_groups) * 8 + xcd;
         qg = slot % n_groups;
-        if (u >= units) return;  // before any barrier: the whole workgroup exits
+        if (u >= units) return;  // uniform over the (one-wave) workgroup
     }
     const int b = u / H;
-
-    // Stage the sequence's cached list (sanitised) in LDS.
-    const int32_t* cidx_g = cached_idx + (size_t)b * ldc;
-    for (int c = lane; c < Nc; c += kWave) {
-        const int n = cidx_g[c];
-        cidx_s[c] = (n >= 0 && n < N) ? n : -1;
-    }
-
-    // Q tile as the B operand of S^T = K Q^T: lane holds query m16 of tile qt,
-    // head-dim elements [8g, 8g+8) (k-step 0) and [32+8g, 32+8g+8) (k-step 1).
     const int q0 = qg * kQueriesPerGroup;
-    bf16x8_t qf[NQT][2];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        const int qi = q0 + qt * 16 + m16;
-        uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
-        if (qi < A) {
-            const uint4* p = reinterpret_cast<const uint4*>(q_a + ((size_t)u * A + qi) * kD);
-            lo = p[g];
-            hi = p[4 + g];
-        }
-        qf[qt][0] = as_bf16x8(lo);
-        qf[qt][1] = as_bf16x8(hi);
-    }
+    const int nq = min(A - q0, 16 * NQT);  // queries of this group (>= 1)
 
-    const uint16_t* ka_u = k_a + (size_t)u * A * kD;
-    const uint16_t* va_u = v_a + (size_t)u * A * kD;
-    const uint16_t* kc_u = k_cache + (size_t)u * N * kD;
-    const uint16_t* vc_u = v_cache + (size_t)u * N * kD;
+    const uint16_t* ka_u = k_a + static_cast<size_t>(u) * A * kD;
+    const uint16_t* va_u = v_a + static_cast<size_t>(u) * A * kD;
+    const uint16_t* kc_u = k_cache + static_cast<size_t>(u) * N * kD;
+    const uint16_t* vc_u = v_cache + static_cast<size_t>(u) * N * kD;
     const int T = A + Nc;
     const int nchunks = (T + kChunk - 1) / kChunk;
 
-    __syncthreads();  // cidx_s visible
-
-    // Loader roles.  K: lane loads row (16t + m16) of the chunk, pieces g and
-    // 4+g (16 bytes each).  V: lane loads row (lane & 31), pieces 4*(lane>>5)+k.
-    const int vrow_l = lane & 31;
-    const int vpiece0 = (lane >> 5) * 4;
-
-    uint4 kA[2][2], kB[2][2], vA[4], vB[4];
-    uint32_t mA[2], mB[2];
-    bool okA, okB;
-
-    // Loads are unconditional: a missing row (past the end, or an invalid
-    // cached index) reads active row 0 instead.  Its scores are masked to
-    // -inf through `mk`, and its V row is replaced by zeros when staged, so
-    // it contributes nothing.
-    auto load_chunk = [&](int c, uint4 (&kr)[2][2], uint4 (&vr)[4], uint32_t (&mk)[2],
-                          bool& vok) {
-        const int base = c * kChunk;
+    // The first entries of the cached list are requested first: they gate
+    // every chunk that holds a cached row.
+    constexpr int kIdxRegs = 8;
+    const int32_t* cidx_g = cached_idx + static_cast<size_t>(b) * ldc;
+    int32_t iv[kIdxRegs];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const RowRef rk = row_ref(base + 16 * t + m16, A, Nc, cidx_s, ka_u, kc_u);
-            const uint4* p = reinterpret_cast<const uint4*>(rk.p);
-            kr[t][0] = p[g];
-            kr[t][1] = p[4 + g];
-            mk[t] = static_cast<uint32_t>(__ballot(rk.ok) & 0xffffull);
-        }
-        const RowRef rv = row_ref(base + vrow_l, A, Nc, cidx_s, va_u, vc_u);
-        const uint4* pv = reinterpret_cast<const uint4*>(rv.p);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) vr[k] = pv[vpiece0 + k];
-        vok = rv.ok;
-    };
+    for (int k = 0; k < kIdxRegs; ++k) {
+        const int c = lane + kWave * k;
+        iv[k] = (c < Nc) ? cidx_g[c] : -1;
+    }
 
-    float mrow[NQT], lrow[NQT];
-    f32x4_t oacc[NQT][4];
+    // Q tile as the B operand of S^T = K Q^T: lane holds query m16 of tile qt,
+    // head dims [8g, 8g+8) (k-step 0) and [32+8g, 32+8g+8) (k-step 1).
+    // Queries past the group's end load its last query; they are never stored.
+    bf16x8_t qf[NQT][2];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-        mrow[qt] = -INFINITY;
-        lrow[qt] = 0.f;
+        const int qi = q0 + min(qt * 16 + m16, nq - 1);
+        const uint4* p = reinterpret_cast<const uint4*>(q_a + (static_cast<size_t>(u) * A + qi) * kD);
+        qf[qt][0] = as_bf16x8(p[g]);
+        qf[qt][1] = as_bf16x8(p[4 + g]);
+    }
+
+    auto issue = [&](int c, ChunkRegs& cr) __attribute__((always_inline)) {
+        const int r0 = c * kChunk;
+        uint32_t valid = 0;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            bool ok;
+            const uint4* p = reinterpret_cast<const uint4*>(
+                row_ptr(r0 + 16 * t + m16, A, Nc, cidx_s, ka_u, kc_u, ok));
+            cr.k[t][0] = p[g];
+            cr.k[t][1] = p[4 + g];
+            valid |= static_cast<uint32_t>(__ballot(ok) & 0xffffull) << (16 * t);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            bool ok;
+            const uint4* p = reinterpret_cast<const uint4*>(
+                row_ptr(r0 + 8 * k + (lane >> 3), A, Nc, cidx_s, va_u, vc_u, ok));
+            cr.v[k] = p[lane & 7];
+        }
+        cr.valid = valid;
+    };
+
+    // Stage the cached list (entries outside [0, N) become -1).
+    auto stage_list = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < kIdxRegs; ++k) {
+            const int c = lane + kWave * k;
+            if (c < Nc) cidx_s[c] = (iv[k] >= 0 && iv[k] < N) ? iv[k] : -1;
+        }
+        for (int c = lane + kWave * kIdxRegs; c < Nc; c += kWave) {
+            const int n = cidx_g[c];
+            cidx_s[c] = (n >= 0 && n < N) ? n : -1;
+        }
+        __syncthreads();  // one wave: orders the list writes before the reads below
+    };
+
+    // Chunk i (i < kPF) starts in cr[i].  A first chunk made only of active
+    // rows does not need the cached list and is requested before it arrives.
+    // When the sequence has fewer than kPF chunks the spare buffers load its
+    // last chunk again (never used), so every path issues the same loads.
+    ChunkRegs cr[kPF + 1];
+    if (A >= kChunk) {
+        issue(0, cr[0]);
+        stage_list();
+    } else {
+        stage_list();
+        issue(0, cr[0]);
+    }
+#pragma unroll
+    for (int k = 1; k < kPF; ++k) issue(min(k, nchunks - 1), cr[k]);
+    // Per-lane LDS byte offsets of the V^T transposing reads: lane s of its
+    // 16-lane group addresses key row 16h + 4g + s/4, head dims 16dt + 4(s%4).
+    int vofs[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            vofs[h][dt] = swz(16 * h + 4 * g + (m16 >> 2), 2 * dt + ((m16 & 3) >> 1)) +
+                          ((m16 & 1) << 3);
+    const int vst = swz(lane >> 3, lane & 7);  // V store slot, + 1024 per 8 rows
+
+    const float thr_raw = kRescaleLog2 / scale_log2;
+    bool tile_on[NQT];
+    float mref[NQT], mc[NQT], mthr[NQT];
+    f32x4_t oacc[NQT][4], lacc[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        tile_on[qt] = qt * 16 < nq;
+        mref[qt] = -INFINITY;
+        mthr[qt] = -INFINITY;
+        mc[qt] = 0.f;
+        lacc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
-    // One chunk: stage its V rows in LDS, start loading chunk c+1 into the
-    // other buffer set (its latency overlaps this chunk's math), then fold the
-    // chunk into the running softmax state.
-    auto step = [&](int c, const uint4 (&kc)[2][2], const uint4 (&vc)[4], const uint32_t (&mk)[2],
-                    bool vok, uint4 (&kn)[2][2], uint4 (&vn)[4], uint32_t (&mn_)[2], bool& vokn) {
+    auto compute = [&](const ChunkRegs& ch) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            *reinterpret_cast<uint4*>(Vs + vrow_l * kVStride + (vpiece0 + k) * 8) =
-                zero_unless(vok, vc[k]);
-        if (c + 1 < nchunks) load_chunk(c + 1, kn, vn, mn_, vokn);
-        __syncthreads();
-
-        // V^T operands: row m16 <-> head dims 4*m16 + dt (dt = output tile),
-        // k-slot j <-> key row 16*(j>>2) + 4g + (j&3) of the chunk; one 8-byte
-        // LDS read per slot serves all four tiles.
+            *reinterpret_cast<uint4*>(tile + vst + 1024 * k) = ch.v[k];
         bf16x8_t va[4];
-        {
-            uint2 w[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int kr = 16 * (j >> 2) + 4 * g + (j & 3);
-                w[j] = *reinterpret_cast<const uint2*>(Vs + kr * kVStride + 4 * m16);
-            }
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                uint32_t e[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t word = (dt < 2) ? w[j].x : w[j].y;
-                    e[j] = (dt & 1) ? (word >> 16) : (word & 0xffffu);
-                }
-                U4 t;
-                t.u = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                                 e[6] | (e[7] << 16));
-                va[dt] = t.v;
-            }
+        for (int dt = 0; dt < 4; ++dt) {
+            const uint2 lo = lds_tr_b64(tile + vofs[0][dt]);
+            const uint2 hi = lds_tr_b64(tile + vofs[1][dt]);
+            va[dt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
-
+        const bool full = ch.valid == 0xffffffffu;  // wave-uniform
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
+            if (!tile_on[qt]) continue;  // wave-uniform
             // S^T tiles: lane holds S^T[key 16t + 4g + i][query m16] in s[t][i].
             f32x4_t s[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[t][0]), qf[qt][0],
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ch.k[t][0]), qf[qt][0],
                                                               acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[t][1]), qf[qt][1],
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ch.k[t][1]), qf[qt][1],
                                                               acc, 0, 0, 0);
                 s[t] = acc;
             }
-            // Online softmax for query m16; P^T packed as the B operand of
-            // O^T = V^T P^T with the same k-slot <-> key row map as va.
-            float v[8];
+            if (!full) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!((ch.valid >> (16 * t + 4 * g + i)) & 1u)) s[t][i] = -INFINITY;
+            }
+            const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+            if (__any(mx > mthr[qt])) {  // a query's maximum moved far up: rescale
+                const float mnew = fmaxf(mref[qt], max_over_groups(mx));
+                const float alpha = (mref[qt] == -INFINITY)
+                                        ? 0.f
+                                        : __builtin_amdgcn_exp2f((mref[qt] - mnew) * scale_log2);
+                lacc[qt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] *= alpha;
+                mref[qt] = mnew;
+                mc[qt] = mnew * scale_log2;
+                mthr[qt] = mnew + thr_raw;
+            }
+            float p[8];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool ok = (mk[t] >> (4 * g + i)) & 1u;
-                    v[4 * t + i] = ok ? s[t][i] * scale_log2 : -INFINITY;
-                }
-            float mx = v[0];
-#pragma unroll
-            for (int k = 1; k < 8; ++k) mx = fmaxf(mx, v[k]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            const float mnew = fmaxf(mrow[qt], mx);
-            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mref);
-            float p[8], ps = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                p[k] = __builtin_amdgcn_exp2f(v[k] - mref);
-                ps += p[k];
-            }
-            lrow[qt] = lrow[qt] * alpha + ps;
-            mrow[qt] = mnew;
+                for (int i = 0; i < 4; ++i)
+                    p[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(s[t][i], scale_log2, -mc[qt]));
             U4 pk;
             pk.u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+            lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk.v, lacc[qt], 0, 0, 0);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                oacc[qt][dt] *= alpha;
-                oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk.v, oacc[qt][dt],
-                                                                       0, 0, 0);
-            }
+            for (int dt = 0; dt < 4; ++dt)
+                oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk.v,
+                                                                       oacc[qt][dt], 0, 0, 0);
         }
-        __syncthreads();  // all V reads done before the next chunk overwrites Vs
     };
 
-    load_chunk(0, kA, vA, mA, okA);
-    for (int c = 0; c < nchunks; c += 2) {
-        step(c, kA, vA, mA, okA, kB, vB, mB, okB);
-        if (c + 1 < nchunks) step(c + 1, kB, vB, mB, okB, kA, vA, mA, okA);
+    // Chunk c lives in cr[c % (kPF + 1)].  Each step requests chunk c + kPF
+    // into the buffer chunk c - 1 just left, then computes chunk c.  Near the
+    // end the request is clamped to the last chunk, which was fetched a moment
+    // earlier and is served by L2: every step then issues the same loads, so
+    // the compiler's memory-counter waits stay exact with kPF chunks in flight
+    // (a conditional request would make them wait for everything).  The loop
+    // is unrolled by kPF + 1 so every register buffer index is a constant.
+    auto step = [&](int c, auto buf_tag) __attribute__((always_inline)) {
+        constexpr int BI = decltype(buf_tag)::value;
+        constexpr int BN = (BI + kPF) % (kPF + 1);
+        issue(min(c + kPF, nchunks - 1), cr[BN]);
+        compute(cr[BI]);
+    };
+    // Whole groups without guards (so the state at the loop back edge is the
+    // same on every path), then the last nchunks mod (kPF + 1) chunks.
+    int c = 0;
+    for (; c + kPF < nchunks; c += kPF + 1) {
+        step(c, std::integral_constant<int, 0>{});
+        step(c + 1, std::integral_constant<int, 1>{});
+        if constexpr (kPF >= 2) step(c + 2, std::integral_constant<int, 2>{});
+        if constexpr (kPF >= 3) step(c + 3, std::integral_constant<int, 3>{});
     }
+    if (c < nchunks) step(c, std::integral_constant<int, 0>{});
+    if constexpr (kPF >= 2)
+        if (c + 1 < nchunks) step(c + 1, std::integral_constant<int, 1>{});
+    if constexpr (kPF >= 3)
+        if (c + 2 < nchunks) step(c + 2, std::integral_constant<int, 2>{});
 
-    // Finalise: lane holds O[query m16][16g + 4i + dt] = oacc[qt][dt][i].
+    // Finalise: lane holds O[query 16qt + m16][16dt + 4g + i] = oacc[qt][dt][i]
+    // and the softmax denominator of that query in every lacc[qt][i].  The
+    // tile goes through LDS (same swizzle) and leaves as whole rows.
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-        float l = lrow[qt];
-        l += __shfl_xor(l, 16, kWave);
-        l += __shfl_xor(l, 32, kWave);
-        const int qi = q0 + qt * 16 + m16;
-        if (qi < A) {
-            const float inv = 1.f / l;
-            uint32_t wv[8];
+        if (!tile_on[qt]) continue;
+        const float l = lacc[qt][0];
+        const float inv = 1.f / l;
+        const int row = 16 * qt + m16;
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                const float lo = oacc[qt][e & 3][e >> 2] * inv;
-                const float hi = oacc[qt][(e + 1) & 3][(e + 1) >> 2] * inv;
-                wv[e / 2] = pack_bf16x2(lo, hi);
-            }
-            uint4* dst = reinterpret_cast<uint4*>(out + ((size_t)u * A + qi) * kD + 16 * g);
-            dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-            dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
-            if (lse != nullptr && g == 0) lse[(size_t)u * A + qi] = (mrow[qt] + log2f(l)) * kLn2;
+        for (int dt = 0; dt < 4; ++dt) {
+            const uint2 w = make_uint2(pack_bf16x2(oacc[qt][dt][0] * inv, oacc[qt][dt][1] * inv),
+                                       pack_bf16x2(oacc[qt][dt][2] * inv, oacc[qt][dt][3] * inv));
+            *reinterpret_cast<uint2*>(tile + swz(row, 2 * dt + (g >> 1)) + ((g & 1) << 3)) = w;
+        }
+        const int qi = q0 + row;
+        if (lse != nullptr && g == 0 && row < nq)
+            lse[static_cast<size_t>(u) * A + qi] = (mc[qt] + log2f(l)) * kLn2;
+    }
+    __syncthreads();
+    u32x4_t* orow = reinterpret_cast<u32x4_t*>(out + (static_cast<size_t>(u) * A + q0) * kD);
+#pragma unroll
+    for (int k = 0; k < 2 * NQT; ++k) {
+        const int row = 8 * k + (lane >> 3);
+        if (row < nq) {
+            const u32x4_t w = *reinterpret_cast<const u32x4_t*>(tile + swz(row, lane & 7));
+            __builtin_nontemporal_store(w, orow + row * 8 + (lane & 7));
         }
     }
 }
@@ -410,13 +506,13 @@ int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
                 int n_groups, float scale_log2, hipStream_t stream) {
     const int units = B * H;
     const int grid = (n_groups == 1) ? units : ((units + 7) / 8) * 8 * n_groups;
-    const size_t lds = (size_t)kChunk * kVStride * 2 + (size_t)(Nc > 0 ? Nc : 1) * 4;
+    constexpr size_t kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
+    const size_t lds = kTileBytes + static_cast<size_t>(Nc > 0 ? Nc : 1) * 4;
     hipLaunchKernelGGL(attn_mfma_kernel<NQT>, dim3(grid), dim3(64), lds, stream, q_a, k_a, v_a,
                        k_cache, v_cache, cached_idx, ldc, out, lse, units, H, N, A, Nc, n_groups,
                        scale_log2);
     return status_from_launch();
 }
-
 }  // namespace
 
 int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a, const void* k_cache,
