@@ -233,6 +233,12 @@ def main():
         marca.mar_kv_scatter_refresh(L["k_cache"], L["v_cache"], L["k_a"], L["v_a"],
                                      x["active_idx"])
 
+    def fused(l, plan):
+        L = x["layers"][l]
+        marca.mar_cache_attn_fwd_update(L["q_a"], L["k_a"], L["v_a"], L["k_cache"],
+                                        L["v_cache"], x["cached_idx"], x["active_idx"],
+                                        Nc=plan.n_cached, out=L["out"])
+
     def cfg_reuse():
         marca.mar_cfg_residual(x["cond"], residual=x["residual"], mode=marca.MAR_CFG_REUSE,
                                uncond_out=x["uncond_out"])
@@ -257,6 +263,15 @@ def main():
         cfg_reuse()
         gate()
 
+    def one_step_fused():
+        """The same step with each layer's attention and cache update in one kernel."""
+        plan = plan_step()
+        topk(plan)
+        for l in range(n_ca):
+            fused(l, plan)
+        cfg_reuse()
+        gate()
+
     def timed_kernels():
         """The same launches as one step, grouped by kernel so that one pair of HIP
         events brackets each group of back-to-back launches (an event pair around
@@ -271,6 +286,7 @@ def main():
         span("topk", lambda: topk(plan), 1)
         span("attn", lambda: [attn(l, plan) for l in range(n_ca)], n_ca)
         span("scatter", lambda: [scatter(l) for l in range(n_ca)], n_ca)
+        span("attn_update", lambda: [fused(l, plan) for l in range(n_ca)], n_ca)
         span("cfg", cfg_reuse, 1)
         span("gate", gate, 1)
         return spans
@@ -293,6 +309,18 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = s0.elapsed_time(s1) / args.steps
 
+    # Timed region 1b: whole steps with the fused attention + cache update.
+    for _ in range(args.warmup):
+        one_step_fused()
+    torch.cuda.synchronize()
+    f0, f1 = ev(), ev()
+    f0.record(stream)
+    for _ in range(args.steps):
+        one_step_fused()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step_fused = f0.elapsed_time(f1) / args.steps
+
     # Timed region 2: the same launches, grouped per kernel, HIP events per group.
     groups = [timed_kernels() for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -304,6 +332,8 @@ def main():
     bytes_call = attn_bytes(cfg.B, cfg.H, cfg.A, cfg.Nc, cfg.D)
     achieved = bytes_call / (avg_us["attn"] * 1e-6) / 1e9
     traffic = load_traffic(bytes_call)
+    bytes_fused = bytes_call + 2 * cfg.B * cfg.H * cfg.A * cfg.D * 2  # + K_A, V_A rows written
+    achieved_fused = bytes_fused / (avg_us["attn_update"] * 1e-6) / 1e9
 
     copy_gbs = None
     try:  # achievable HBM: the plain full-refresh copy over one layer's caches
@@ -339,6 +369,14 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": cpu,
         "kernel_us": avg_us,
+        "fused_step": {
+            "what": "the same step with mar_cache_attn_fwd_update (attention + cache update of "
+                    "the active rows in one kernel) in place of attention + scatter",
+            "ms_per_step": ms_per_step_fused,
+            "value": tokens_per_step / (ms_per_step_fused * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": achieved_fused, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": achieved_fused / PEAK_HBM_GBS,
+                         "bytes_per_call": bytes_fused}},
         "attn_bytes_per_call": bytes_call,
         "attn_tok_per_s": cfg.B * cfg.A / (avg_us["attn"] * 1e-6),
         "copy_gbs": copy_gbs,

@@ -60,6 +60,9 @@ def load_library(path: Optional[str] = None):
     lib.mar_version.restype = I
     lib.mar_cache_attn_fwd.restype = I
     lib.mar_cache_attn_fwd.argtypes = [V, V, V, V, V, V, I, V, V, I, I, I, I, I, I, F, I, V]
+    lib.mar_cache_attn_fwd_update.restype = I
+    lib.mar_cache_attn_fwd_update.argtypes = [V, V, V, V, V, V, I, V, I, V, V, V, I, I, I, I, I,
+                                              I, F, I, V]
     lib.mar_kv_scatter_refresh.restype = I
     lib.mar_kv_scatter_refresh.argtypes = [V, V, V, V, V, I, V, I, I, I, I, I, I, V]
     lib.mar_refresh_topk_workspace.restype = S
@@ -146,6 +149,52 @@ def mar_cache_attn_fwd(q_a, k_a, v_a, k_cache, v_cache, cached_idx, Nc=None, out
         _dev(lse, "lse") if lse is not None else None, B, H, N, A, Nc, D, float(scale), code,
         _stream(stream))
     _check("mar_cache_attn_fwd", st)
+    return out
+
+
+def mar_cache_attn_fwd_update(q_a, k_a, v_a, k_cache, v_cache, cached_idx, active_idx, Nc=None,
+                              out=None, lse=None, err_count=None, scale=None, stream=None):
+    """mar_cache_attn_fwd, plus k_cache/v_cache rows at active_idx [B, ld] (first A
+    entries) overwritten with k_a/v_a in the same pass.  Returns out."""
+    B, H, A, D = q_a.shape
+    N = k_cache.shape[2]
+    dt = q_a.dtype
+    code = _dtype_code(q_a)
+    for name, t in (("k_a", k_a), ("v_a", v_a)):
+        _dev(t, name, dt, (B, H, A, D))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, name, dt, (B, H, N, D))
+    if cached_idx is None:
+        ldc, Nc = 0, 0 if Nc is None else Nc
+        cptr = None
+    else:
+        if cached_idx.dim() != 2 or cached_idx.shape[0] != B:
+            raise ValueError("cached_idx must be [B, ldc]")
+        ldc = cached_idx.shape[1]
+        Nc = ldc if Nc is None else int(Nc)
+        cptr = _dev(cached_idx, "cached_idx", torch.int32)
+    if active_idx.dim() != 2 or active_idx.shape[0] != B or active_idx.stride(1) != 1:
+        raise ValueError("active_idx must be [B, ld] with unit column stride")
+    ld_act = active_idx.stride(0)
+    aptr = ctypes.c_void_p(active_idx.data_ptr())
+    if active_idx.dtype != torch.int32 or not active_idx.is_cuda:
+        raise ValueError("active_idx must be an int32 device tensor")
+    if out is None:
+        out = torch.empty_like(q_a)
+    _dev(out, "out", dt, (B, H, A, D))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, H, A))
+    if err_count is not None:
+        _dev(err_count, "err_count", torch.int32)
+    if scale is None:
+        scale = D ** -0.5
+    st = load_library().mar_cache_attn_fwd_update(
+        _dev(q_a, "q_a"), _dev(k_a, "k_a"), _dev(v_a, "v_a"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), cptr, ldc, aptr, ld_act,
+        _dev(err_count, "err_count") if err_count is not None else None, _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else None, B, H, N, A, Nc, D, float(scale), code,
+        _stream(stream))
+    _check("mar_cache_attn_fwd_update", st)
     return out
 
 

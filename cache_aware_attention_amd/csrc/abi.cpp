@@ -34,23 +34,50 @@ extern "C" const char* mar_status_string(int status) {
 
 extern "C" int mar_version(void) { return 100; }
 
-extern "C" int mar_cache_attn_fwd(const void* q_a, const void* k_a, const void* v_a,
-                                  const void* k_cache, const void* v_cache,
-                                  const int32_t* cached_idx, int ldc, void* out, float* lse,
-                                  int B, int H, int N, int A, int Nc, int D, float scale,
-                                  int dtype, void* stream) {
+static int check_cache_attn(const void* q_a, const void* k_a, const void* v_a,
+                            const void* k_cache, const void* v_cache, const int32_t* cached_idx,
+                            int ldc, const void* out, int B, int H, int N, int A, int Nc, int D,
+                            float scale, int dtype) {
     if (!q_a || !k_a || !v_a || !k_cache || !v_cache || !out) return MAR_E_NULL;
     if (Nc > 0 && !cached_idx) return MAR_E_NULL;
     if (elem_bytes(dtype) == 0) return MAR_E_DTYPE;
     if (B < 1 || H < 1 || N < 1 || A < 1 || D < 1 || Nc < 0) return MAR_E_SHAPE;
     if ((long long)A + Nc > N || (Nc > 0 && ldc < Nc)) return MAR_E_SHAPE;
     if (D != kHeadDim) return MAR_E_UNSUPPORTED;
-    if (!(scale == scale)) return MAR_E_RANGE;
+    if (!(scale > 0.f) || scale > 3.0e38f) return MAR_E_RANGE;  // positive and finite
     if (!aligned16(q_a) || !aligned16(k_a) || !aligned16(v_a) || !aligned16(k_cache) ||
         !aligned16(v_cache) || !aligned16(out))
         return MAR_E_RANGE;
+    return MAR_OK;
+}
+
+extern "C" int mar_cache_attn_fwd(const void* q_a, const void* k_a, const void* v_a,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* cached_idx, int ldc, void* out, float* lse,
+                                  int B, int H, int N, int A, int Nc, int D, float scale,
+                                  int dtype, void* stream) {
+    const int st = check_cache_attn(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, B, H,
+                                    N, A, Nc, D, scale, dtype);
+    if (st != MAR_OK) return st;
     return marca::launch_cache_attn(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
                                     B, H, N, A, Nc, scale, dtype, stream);
+}
+
+extern "C" int mar_cache_attn_fwd_update(const void* q_a, const void* k_a, const void* v_a,
+                                         void* k_cache, void* v_cache,
+                                         const int32_t* cached_idx, int ldc,
+                                         const int32_t* active_idx, int ld_act,
+                                         int32_t* err_count, void* out, float* lse, int B, int H,
+                                         int N, int A, int Nc, int D, float scale, int dtype,
+                                         void* stream) {
+    if (!active_idx) return MAR_E_NULL;
+    const int st = check_cache_attn(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, B, H,
+                                    N, A, Nc, D, scale, dtype);
+    if (st != MAR_OK) return st;
+    if (ld_act < A) return MAR_E_SHAPE;
+    return marca::launch_cache_attn_update(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc,
+                                           active_idx, ld_act, err_count, out, lse, B, H, N, A,
+                                           Nc, scale, dtype, stream);
 }
 
 extern "C" int mar_kv_scatter_refresh(void* k_cache, void* v_cache, const void* k_new,

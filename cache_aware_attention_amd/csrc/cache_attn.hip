@@ -232,20 +232,27 @@ struct ChunkRegs {
     uint32_t valid;  // bit j: key row j of the chunk exists (wave-uniform)
 };
 
-template <int NQT>
+// UPDATE: also write the unit's fresh active K/V rows into the caches at
+// their token positions (active_idx), from the registers that already hold
+// them for the attention.  The rows read from the caches are the cached set,
+// which is disjoint from the active positions, so the reads and the writes of
+// one unit never touch the same row and different units never share a row.
+template <int NQT, bool UPDATE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
-                      const uint16_t* __restrict__ v_a, const uint16_t* __restrict__ k_cache,
-                      const uint16_t* __restrict__ v_cache,
-                      const int32_t* __restrict__ cached_idx, int ldc,
+                      const uint16_t* __restrict__ v_a, const uint16_t* k_cache,
+                      const uint16_t* v_cache, const int32_t* __restrict__ cached_idx, int ldc,
                       uint16_t* __restrict__ out, float* __restrict__ lse, int units, int H,
-                      int N, int A, int Nc, int n_groups, float scale_log2) {
+                      int N, int A, int Nc, int n_groups, float scale_log2,
+                      const int32_t* __restrict__ active_idx, int ld_act,
+                      int32_t* __restrict__ err_count) {
     constexpr int kPF = prefetch_depth(NQT);
     static_assert(kPF >= 1 && kPF <= 3, "prefetch depth");
     constexpr int kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* tile = smem;  // V chunk, later the output tile
     int32_t* cidx_s = reinterpret_cast<int32_t*>(smem + kTileBytes);  // [max(Nc, 1)]
+    int32_t* aidx_s = cidx_s + (Nc > 0 ? Nc : 1);                     // [A] with UPDATE
 
     const int lane = threadIdx.x;
     const int g = lane >> 4;    // lane group: k-slot group of the MFMA operands
@@ -332,6 +339,17 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
             const int n = cidx_g[c];
             cidx_s[c] = (n >= 0 && n < N) ? n : -1;
         }
+        if constexpr (UPDATE) {
+            // Only the first query group of a unit writes its rows.  An entry
+            // outside [0, N) is skipped and, once per sequence, counted.
+            const int32_t* ag = active_idx + static_cast<size_t>(b) * ld_act;
+            for (int r = lane; r < A; r += kWave) {
+                const int n = ag[r];
+                const bool ok = n >= 0 && n < N;
+                aidx_s[r] = (ok && qg == 0) ? n : -1;
+                if (!ok && err_count != nullptr && qg == 0 && u % H == 0) atomicAdd(err_count, 1);
+            }
+        }
         __syncthreads();  // one wave: orders the list writes before the reads below
     };
 
@@ -376,10 +394,40 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     }
     const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
-    auto compute = [&](const ChunkRegs& ch) __attribute__((always_inline)) {
+    auto compute = [&](int c, const ChunkRegs& ch) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             *reinterpret_cast<uint4*>(tile + vst + 1024 * k) = ch.v[k];
+        if constexpr (UPDATE) {
+            if (c * kChunk < A) {  // wave-uniform: the chunk holds active rows
+                // Buffer stores: an offset past the unit's N rows (inactive
+                // lane, skipped entry) is dropped by the range check.
+                constexpr uint32_t kSkip = 0x80000000u;
+                constexpr int kNT = 2;  // cache-policy bits: nontemporal (streaming) store
+                const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint16_t*>(kc_u), 0, N * kD * 2, 0x00020000);
+                const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint16_t*>(vc_u), 0, N * kD * 2, 0x00020000);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int r = c * kChunk + 16 * t + m16;
+                    const int n = (r < A) ? aidx_s[r] : -1;
+                    const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.k[t][0]),
+                                                           rk, off + 16 * g, 0, kNT);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.k[t][1]),
+                                                           rk, off + 16 * (4 + g), 0, kNT);
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int r = c * kChunk + 8 * k + (lane >> 3);
+                    const int n = (r < A) ? aidx_s[r] : -1;
+                    const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.v[k]),
+                                                           rv, off + 16 * (lane & 7), 0, kNT);
+                }
+            }
+        }
         bf16x8_t va[4];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
@@ -451,7 +499,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         constexpr int BI = decltype(buf_tag)::value;
         constexpr int BN = (BI + kPF) % (kPF + 1);
         issue(min(c + kPF, nchunks - 1), cr[BN]);
-        compute(cr[BI]);
+        compute(c, cr[BI]);
     };
     // Whole groups without guards (so the state at the loop back edge is the
     // same on every path), then the last nchunks mod (kPF + 1) chunks.
@@ -499,20 +547,50 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     }
 }
 
-template <int NQT>
+template <int NQT, bool UPDATE>
 int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
                 const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* cached_idx,
                 int ldc, uint16_t* out, float* lse, int B, int H, int N, int A, int Nc,
-                int n_groups, float scale_log2, hipStream_t stream) {
+                int n_groups, float scale_log2, const int32_t* active_idx, int ld_act,
+                int32_t* err_count, hipStream_t stream) {
     const int units = B * H;
     const int grid = (n_groups == 1) ? units : ((units + 7) / 8) * 8 * n_groups;
     constexpr size_t kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
-    const size_t lds = kTileBytes + static_cast<size_t>(Nc > 0 ? Nc : 1) * 4;
-    hipLaunchKernelGGL(attn_mfma_kernel<NQT>, dim3(grid), dim3(64), lds, stream, q_a, k_a, v_a,
-                       k_cache, v_cache, cached_idx, ldc, out, lse, units, H, N, A, Nc, n_groups,
-                       scale_log2);
+    const size_t lds = kTileBytes + static_cast<size_t>(Nc > 0 ? Nc : 1) * 4 +
+                       (UPDATE ? static_cast<size_t>(A) * 4 : 0);
+    hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE>), dim3(grid), dim3(64), lds, stream, q_a,
+                       k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse, units, H, N, A, Nc,
+                       n_groups, scale_log2, active_idx, ld_act, err_count);
     return status_from_launch();
 }
+
+template <bool UPDATE>
+int dispatch_mfma(const uint16_t* q, const uint16_t* ka, const uint16_t* va, const uint16_t* kc,
+                  const uint16_t* vc, const int32_t* cached_idx, int ldc, uint16_t* o, float* lse,
+                  int B, int H, int N, int A, int Nc, float scale_log2, const int32_t* active_idx,
+                  int ld_act, int32_t* err_count, hipStream_t stream) {
+    const int n_groups = (A + kQueriesPerGroup - 1) / kQueriesPerGroup;
+    const int nqt = (n_groups > 1) ? 4 : (A + 15) / 16;
+    switch (nqt) {
+        case 1:
+            return launch_mfma<1, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
+                                          Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
+                                          stream);
+        case 2:
+            return launch_mfma<2, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
+                                          Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
+                                          stream);
+        case 3:
+            return launch_mfma<3, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
+                                          Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
+                                          stream);
+        default:
+            return launch_mfma<4, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
+                                          Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
+                                          stream);
+    }
+}
+
 }  // namespace
 
 int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a, const void* k_cache,
@@ -529,14 +607,8 @@ int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a, const v
         const uint16_t* kc = static_cast<const uint16_t*>(k_cache);
         const uint16_t* vc = static_cast<const uint16_t*>(v_cache);
         uint16_t* o = static_cast<uint16_t*>(out);
-        const int n_groups = (A + kQueriesPerGroup - 1) / kQueriesPerGroup;
-        const int nqt = (n_groups > 1) ? 4 : (A + 15) / 16;
-        switch (nqt) {
-            case 1: return launch_mfma<1>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A, Nc, n_groups, scale_log2, stream);
-            case 2: return launch_mfma<2>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A, Nc, n_groups, scale_log2, stream);
-            case 3: return launch_mfma<3>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A, Nc, n_groups, scale_log2, stream);
-            default: return launch_mfma<4>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A, Nc, n_groups, scale_log2, stream);
-        }
+        return dispatch_mfma<false>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A, Nc,
+                                    scale_log2, nullptr, 0, nullptr, stream);
     }
     const dim3 grid(B * H, (A + 3) / 4);
     if (dtype == MAR_BF16) {
@@ -553,6 +625,30 @@ int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a, const v
                            static_cast<float*>(out), lse, H, N, A, Nc, scale_log2);
     }
     return status_from_launch();
+}
+
+int launch_cache_attn_update(const void* q_a, const void* k_a, const void* v_a, void* k_cache,
+                             void* v_cache, const int32_t* cached_idx, int ldc,
+                             const int32_t* active_idx, int ld_act, int32_t* err_count, void* out,
+                             float* lse, int B, int H, int N, int A, int Nc, float scale,
+                             int dtype, void* stream_v) {
+    if (dtype == MAR_BF16 && A >= 16 && N <= kMaxMfmaTokens) {
+        if (cached_idx == nullptr) ldc = 0;
+        return dispatch_mfma<true>(
+            static_cast<const uint16_t*>(q_a), static_cast<const uint16_t*>(k_a),
+            static_cast<const uint16_t*>(v_a), static_cast<const uint16_t*>(k_cache),
+            static_cast<const uint16_t*>(v_cache), cached_idx, ldc, static_cast<uint16_t*>(out),
+            lse, B, H, N, A, Nc, scale * kLog2e, active_idx, ld_act, err_count,
+            static_cast<hipStream_t>(stream_v));
+    }
+    // Row-wise path: the attention, then the row scatter on the same stream
+    // (the two touch disjoint cache rows, so the order does not matter).
+    const int st = launch_cache_attn(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
+                                     B, H, N, A, Nc, scale, dtype, stream_v);
+    if (st != MAR_OK) return st;
+    const int row_bytes = kD * (dtype == MAR_BF16 ? 2 : 4);
+    return launch_kv_scatter(k_cache, v_cache, k_a, v_a, active_idx, ld_act, err_count, B, H, N,
+                             A, row_bytes, stream_v);
 }
 
 }  // namespace marca

@@ -79,7 +79,8 @@ int mar_version(void);
  *                     writes) is skipped, never read out of bounds.
  *   out               [B,H,A,D]  same dtype as the inputs
  *   lse               [B,H,A] float, may be NULL
- *   scale             usually 1/sqrt(D)
+ *   scale             softmax temperature, positive and finite (usually 1/sqrt(D));
+ *                     MAR_E_RANGE otherwise
  * Requires 1 <= A, 0 <= Nc, A + Nc <= N, ldc >= Nc, D == 64 (else
  * MAR_E_UNSUPPORTED).  Nc == 0 is plain attention over the active set (A == N
  * is the full-attention layer).  The output does not depend on the order of
@@ -91,6 +92,35 @@ int mar_cache_attn_fwd(const void* q_a, const void* k_a, const void* v_a,
                        void* out, float* lse,
                        int B, int H, int N, int A, int Nc, int D,
                        float scale, int dtype, void* stream);
+
+/*
+ * Cache-aware attention fused with the cache update of the active rows
+ * ([MARche] Overall Architecture: attention over the active and cached sets
+ * as one fused operator; abstract on the Pith page: only the recomputed
+ * tokens' cache entries are updated).
+ *
+ * Computes exactly what mar_cache_attn_fwd computes and, in the same pass,
+ * writes the fresh active rows into the caches:
+ *   k_cache[b,h,active_idx[b*ld_act+i],:] = k_a[b,h,i,:]  (and V),  i < A
+ * -- the partial update of mar_kv_scatter_refresh with idx = active_idx and
+ * M = A -- from the registers that already hold those rows, so the rows are
+ * read from memory once.
+ *   active_idx  [B,ld_act] int32: token positions of the A active rows.
+ *   err_count   device int32, may be NULL: +1 per (sequence, entry) outside
+ *               [0,N); such entries are skipped.
+ * Precondition: the active positions of a sequence are distinct and none of
+ * them is among its first Nc cached entries (the cached set is the
+ * complement of the active set), so no cache row is both read and written;
+ * otherwise the value read for such a row is unspecified.  Requirements and
+ * errors as for mar_cache_attn_fwd, plus active_idx != NULL, ld_act >= A.
+ */
+int mar_cache_attn_fwd_update(const void* q_a, const void* k_a, const void* v_a,
+                              void* k_cache, void* v_cache,
+                              const int32_t* cached_idx, int ldc,
+                              const int32_t* active_idx, int ld_act, int32_t* err_count,
+                              void* out, float* lse,
+                              int B, int H, int N, int A, int Nc, int D,
+                              float scale, int dtype, void* stream);
 
 /*
  * KV cache update  ([MARche] abstract on the Pith page: only the tokens that

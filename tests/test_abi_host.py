@@ -67,7 +67,28 @@ def test_cache_attn_rejections(lib):
     assert attn(lib, ldc=100) == E_SHAPE           # ldc < Nc
     assert attn(lib, D=128) == E_UNSUP
     assert attn(lib, scale=float("nan")) == E_RANGE
+    assert attn(lib, scale=0.0) == E_RANGE
+    assert attn(lib, scale=-0.125) == E_RANGE
+    assert attn(lib, scale=float("inf")) == E_RANGE
     assert attn(lib, kc=BAD) == E_RANGE            # misaligned
+
+
+def attn_upd(lib, q=P, ka=P, va=P, kc=P, vc=P, cidx=P, ldc=272, aidx=P, ld_act=48, err=None,
+             out=P, lse=None, B=2, H=2, N=320, A=48, Nc=272, D=64, scale=0.125, dtype=1):
+    return lib.mar_cache_attn_fwd_update(q, ka, va, kc, vc, cidx, ldc, aidx, ld_act, err, out, lse,
+                                         B, H, N, A, Nc, D, scale, dtype, None)
+
+
+def test_cache_attn_update_rejections(lib):
+    assert attn_upd(lib, aidx=None) == E_NULL       # the active list is required
+    assert attn_upd(lib, ld_act=47) == E_SHAPE      # ld_act < A
+    assert attn_upd(lib, q=None) == E_NULL          # the attention's own checks apply
+    assert attn_upd(lib, cidx=None) == E_NULL
+    assert attn_upd(lib, A=49) == E_SHAPE
+    assert attn_upd(lib, D=128) == E_UNSUP
+    assert attn_upd(lib, scale=-1.0) == E_RANGE
+    assert attn_upd(lib, kc=BAD) == E_RANGE
+    assert attn_upd(lib, dtype=3) == E_DTYPE
 
 
 def test_scatter_rejections(lib):
