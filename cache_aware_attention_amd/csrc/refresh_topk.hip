@@ -8,14 +8,16 @@
 // Overall Architecture: active = generating + caching + refreshing tokens,
 // cached = every other token.
 //
-// Kernel 1 (one workgroup per (sequence, head)): two passes over the head's
-// keys -- pass 1 builds each query's softmax max and normaliser with the
-// running (max, sum) rule, pass 2 sums the normalised probabilities over the
-// queries into a per-(b,h,token) partial.  bf16 runs the score tiles on MFMA;
-// fp32 uses a plain FMA version.
+// Kernel 1 (one workgroup per (sequence, head)) writes each token's
+// probability summed over the generating queries into a per-(b,h,token)
+// partial.  bf16: the score tiles run on MFMA; when the head's [queries x
+// keys] score block fits in LDS the keys are read once (scores kept in LDS,
+// then per-query max / sum, then per-key sums), otherwise two passes over
+// the keys (running (max, sum) per query, then normalised sums).  fp32 uses a
+// plain FMA version.
 // Kernel 2 (one workgroup per sequence): sums the partials over heads in a
-// fixed order (no float atomics, deterministic), ranks the eligible tokens
-// with a bitonic sort of 64-bit keys (orderable score << 32 | ~index, so equal
+// fixed order (no float atomics, deterministic), ranks the eligible tokens by
+// counting larger 64-bit keys (orderable score << 32 | ~index, so equal
 // scores put the lower index first), emits the refreshing tokens, and
 // compacts the ascending cached complement with a block prefix sum.
 #include "device_util.h"
@@ -26,6 +28,7 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kThreads = 256;
+constexpr size_t kMaxScoreLds = 64 * 1024;  // single-pass scores when [QT*16][N+16] floats fit
 
 // Merge two running softmax states (max m, sum l) in base 2.
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
@@ -214,71 +217,159 @@ __global__ __launch_bounds__(kThreads) void refresh_scores_mfma_kernel(
     }
 }
 
+// Single-pass bf16 path of kernel 1, used when the head's score block fits
+// in LDS: every wave computes S = Q K^T for its key tiles on MFMA (as above)
+// and writes scale_log2 * S to LDS ([query][key], row stride NS = N + 16
+// floats so the four lane groups of a tile store hit different banks); then
+// one wave per query reduces its row to (max, 1/sum); then one thread per
+// key sums exp2(S - max) / sum over the queries.  Each key row is read from
+// HBM once.
+template <int QT>
+__global__ __launch_bounds__(kThreads) void refresh_scores_lds_kernel(
+    const uint16_t* __restrict__ q_gen, const uint16_t* __restrict__ k_full,
+    float* __restrict__ ws, int G, int N, int NS, float scale_log2) {
+    constexpr int kWaves = kThreads / kWave;
+    constexpr int kBatch = 4;  // key tiles whose loads a wave issues together
+    extern __shared__ float s_lds[];  // [QT * 16][NS]
+    __shared__ float stat_m[QT * 16], stat_inv[QT * 16];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int g = lane >> 4, m16 = lane & 15;
+    const int u = blockIdx.x;
+
+    bf16x8_t qa[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int q = qt * 16 + m16;
+        uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+        if (q < G) {
+            const uint4* p = reinterpret_cast<const uint4*>(q_gen + ((size_t)u * G + q) * kD);
+            lo = p[g];
+            hi = p[4 + g];
+        }
+        qa[qt][0] = __builtin_bit_cast(bf16x8_t, lo);
+        qa[qt][1] = __builtin_bit_cast(bf16x8_t, hi);
+    }
+    const uint16_t* K = k_full + (size_t)u * N * kD;
+    const int ntiles = (N + 15) / 16;
+
+    for (int t0 = w; t0 < ntiles; t0 += kWaves * kBatch) {
+        uint4 kr[kBatch][2];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {  // missing tiles / keys read key row 0
+            const int key = 16 * (t0 + kWaves * b) + m16;
+            const uint4* p = reinterpret_cast<const uint4*>(K + (size_t)(key < N ? key : 0) * kD);
+            kr[b][0] = p[g];
+            kr[b][1] = p[4 + g];
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int t = t0 + kWaves * b;
+            const int key = 16 * t + m16;
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    qa[qt][0], __builtin_bit_cast(bf16x8_t, kr[b][0]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    qa[qt][1], __builtin_bit_cast(bf16x8_t, kr[b][1]), acc, 0, 0, 0);
+                if (t < ntiles && key < N) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s_lds[(qt * 16 + 4 * g + i) * NS + key] = acc[i] * scale_log2;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    for (int q = w; q < G; q += kWaves) {
+        const float* row = s_lds + (size_t)q * NS;
+        float m = -INFINITY;
+        for (int j = lane; j < N; j += kWave) m = fmaxf(m, row[j]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int j = lane; j < N; j += kWave) l += __builtin_amdgcn_exp2f(row[j] - m);
+        l = wave_sum(l);
+        if (lane == 0) {
+            stat_m[q] = m;
+            stat_inv[q] = 1.f / l;
+        }
+    }
+    __syncthreads();
+
+    for (int j = tid; j < N; j += kThreads) {
+        float col = 0.f;
+        for (int q = 0; q < G; ++q)
+            col += __builtin_amdgcn_exp2f(s_lds[(size_t)q * NS + j] - stat_m[q]) * stat_inv[q];
+        ws[(size_t)u * N + j] = col;
+    }
+}
+
 __device__ __forceinline__ uint64_t rank_key(float s, int j) {
     const uint32_t u = __float_as_uint(s);
     const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     return (static_cast<uint64_t>(ord) << 32) | static_cast<uint64_t>(0xffffffffu - (uint32_t)j);
 }
 
+// Kernel 2.  The rank of an eligible token is the number of eligible tokens
+// whose 64-bit key is larger; keys are unique (the index is part of the key),
+// so ranks are a permutation and the K smallest ranks are the refreshing
+// tokens in (score descending, index ascending) order.  Each thread ranks
+// kPerThread tokens against every key held in LDS.
+constexpr int kPerThread = 4;
 __global__ __launch_bounds__(kThreads) void refresh_select_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ gp_idx, int ld_gp, int n_gp, int K,
     float inv_hg, float* __restrict__ scores, int32_t* __restrict__ active_idx, int ld_act,
     int32_t* __restrict__ cached_idx, int ld_cached, int32_t* __restrict__ cached_len, int H,
-    int N, int NP) {
+    int N) {
     extern __shared__ __align__(16) unsigned char smem[];
-    uint64_t* keys = reinterpret_cast<uint64_t*>(smem);    // [NP]
-    uint8_t* state = smem + (size_t)NP * sizeof(uint64_t);  // [N]: 0 cand, 1 G/P, 2 refresh
+    uint64_t* keys = reinterpret_cast<uint64_t*>(smem);   // [N], 0 = not eligible
+    uint8_t* state = smem + (size_t)N * sizeof(uint64_t);  // [N]: 0 cand, 1 G/P, 2 refresh
     __shared__ int scan_scratch[kThreads / kWave];
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
+    int32_t* arow = active_idx + (size_t)b * ld_act;
 
     for (int j = tid; j < N; j += kThreads) state[j] = 0;
+    for (int r = tid; r < K; r += kThreads) arow[n_gp + r] = -1;  // fewer eligible than K
     __syncthreads();
     for (int m = tid; m < n_gp; m += kThreads) {
         const int j = gp_idx[(size_t)b * ld_gp + m];
-        active_idx[(size_t)b * ld_act + m] = j;
+        arow[m] = j;
         if (j >= 0 && j < N) state[j] = 1;
     }
     __syncthreads();
-    for (int j = tid; j < NP; j += kThreads) {
-        uint64_t key = 0;
-        if (j < N) {
-            float s = 0.f;
-            for (int h = 0; h < H; ++h) s += ws[((size_t)b * H + h) * N + j];
-            s *= inv_hg;
-            scores[(size_t)b * N + j] = s;
-            if (state[j] == 0) key = rank_key(s, j);
-        }
-        keys[j] = key;
+    for (int j = tid; j < N; j += kThreads) {
+        float s = 0.f;
+        for (int h = 0; h < H; ++h) s += ws[((size_t)b * H + h) * N + j];
+        s *= inv_hg;
+        scores[(size_t)b * N + j] = s;
+        keys[j] = (state[j] == 0) ? rank_key(s, j) : 0ull;
     }
     __syncthreads();
 
-    // Bitonic sort, descending.
-    for (int k = 2; k <= NP; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < NP; i += kThreads) {
-                const int ixj = i ^ jj;
-                if (ixj > i) {
-                    const uint64_t a = keys[i], c = keys[ixj];
-                    const bool first_half = (i & k) == 0;
-                    if (first_half ? (a < c) : (a > c)) {
-                        keys[i] = c;
-                        keys[ixj] = a;
-                    }
-                }
+    for (int j0 = tid * kPerThread; j0 < N; j0 += kThreads * kPerThread) {
+        uint64_t mine[kPerThread];
+        int rank[kPerThread];
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+            mine[e] = (j0 + e < N) ? keys[j0 + e] : 0ull;
+            rank[e] = 0;
+        }
+        for (int i = 0; i < N; ++i) {
+            const uint64_t other = keys[i];
+#pragma unroll
+            for (int e = 0; e < kPerThread; ++e) rank[e] += (other > mine[e]) ? 1 : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+            if (mine[e] != 0 && rank[e] < K) {
+                arow[n_gp + rank[e]] = j0 + e;
+                state[j0 + e] = 2;
             }
-            __syncthreads();
         }
-    }
-
-    for (int r = tid; r < K; r += kThreads) {
-        const uint64_t key = keys[r];
-        int j = -1;
-        if (key != 0) {
-            j = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-            state[j] = 2;
-        }
-        active_idx[(size_t)b * ld_act + n_gp + r] = j;
     }
     __syncthreads();
 
@@ -313,11 +404,24 @@ int launch_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp
     if (dtype == MAR_BF16) {
         const int qt = (G + 15) / 16;
         const dim3 grid(B * H), block(kThreads);
-        switch (qt) {
-            case 1: hipLaunchKernelGGL(refresh_scores_mfma_kernel<1>, grid, block, 0, stream, static_cast<const uint16_t*>(q_gen), static_cast<const uint16_t*>(k_full), workspace, G, N, scale_log2); break;
-            case 2: hipLaunchKernelGGL(refresh_scores_mfma_kernel<2>, grid, block, 0, stream, static_cast<const uint16_t*>(q_gen), static_cast<const uint16_t*>(k_full), workspace, G, N, scale_log2); break;
-            case 3: hipLaunchKernelGGL(refresh_scores_mfma_kernel<3>, grid, block, 0, stream, static_cast<const uint16_t*>(q_gen), static_cast<const uint16_t*>(k_full), workspace, G, N, scale_log2); break;
-            default: hipLaunchKernelGGL(refresh_scores_mfma_kernel<4>, grid, block, 0, stream, static_cast<const uint16_t*>(q_gen), static_cast<const uint16_t*>(k_full), workspace, G, N, scale_log2); break;
+        const uint16_t* q = static_cast<const uint16_t*>(q_gen);
+        const uint16_t* k = static_cast<const uint16_t*>(k_full);
+        const int NS = N + 16;
+        const size_t lds_s = (size_t)qt * 16 * NS * sizeof(float);
+        if (lds_s <= kMaxScoreLds) {
+            switch (qt) {
+                case 1: hipLaunchKernelGGL(refresh_scores_lds_kernel<1>, grid, block, lds_s, stream, q, k, workspace, G, N, NS, scale_log2); break;
+                case 2: hipLaunchKernelGGL(refresh_scores_lds_kernel<2>, grid, block, lds_s, stream, q, k, workspace, G, N, NS, scale_log2); break;
+                case 3: hipLaunchKernelGGL(refresh_scores_lds_kernel<3>, grid, block, lds_s, stream, q, k, workspace, G, N, NS, scale_log2); break;
+                default: hipLaunchKernelGGL(refresh_scores_lds_kernel<4>, grid, block, lds_s, stream, q, k, workspace, G, N, NS, scale_log2); break;
+            }
+        } else {
+            switch (qt) {
+                case 1: hipLaunchKernelGGL(refresh_scores_mfma_kernel<1>, grid, block, 0, stream, q, k, workspace, G, N, scale_log2); break;
+                case 2: hipLaunchKernelGGL(refresh_scores_mfma_kernel<2>, grid, block, 0, stream, q, k, workspace, G, N, scale_log2); break;
+                case 3: hipLaunchKernelGGL(refresh_scores_mfma_kernel<3>, grid, block, 0, stream, q, k, workspace, G, N, scale_log2); break;
+                default: hipLaunchKernelGGL(refresh_scores_mfma_kernel<4>, grid, block, 0, stream, q, k, workspace, G, N, scale_log2); break;
+            }
         }
     } else {
         hipLaunchKernelGGL(refresh_scores_f32_kernel, dim3(B * H), dim3(kThreads), lds1, stream,
@@ -326,13 +430,11 @@ int launch_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp
     }
     int st = status_from_launch();
     if (st != MAR_OK) return st;
-    int NP = 1;
-    while (NP < N) NP <<= 1;
-    const size_t lds2 = (size_t)NP * sizeof(uint64_t) + (size_t)N;
+    const size_t lds2 = (size_t)N * sizeof(uint64_t) + (size_t)N;
     const float inv_hg = 1.f / (float)(H * G);
     hipLaunchKernelGGL(refresh_select_kernel, dim3(B), dim3(kThreads), lds2, stream, workspace,
                        gp_idx, ld_gp, n_gp, K, inv_hg, scores, active_idx, ld_act, cached_idx,
-                       ld_cached, cached_len, H, N, NP);
+                       ld_cached, cached_len, H, N);
     return status_from_launch();
 }
 

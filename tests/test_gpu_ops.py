@@ -126,7 +126,8 @@ def check_topk(q, k, gp, scores, act, cac, clen, K):
 @pytest.mark.parametrize("B,H,G,N,n_gp,K,dtype", [
     (3, 2, 5, 70, 9, 7, "bf16"), (2, 3, 1, 33, 0, 4, "f32"), (2, 2, 16, 320, 32, 16, "bf16"),
     (2, 2, 17, 100, 20, 30, "bf16"), (1, 4, 40, 257, 60, 40, "f32"), (2, 1, 3, 64, 10, 0, "bf16"),
-    (2, 2, 26, 1088, 52, 76, "bf16")])
+    (2, 2, 26, 1088, 52, 76, "bf16"), (1, 2, 64, 200, 10, 20, "bf16"),
+    (1, 2, 64, 300, 10, 20, "bf16")])
 def test_topk_small(marca, B, H, G, N, n_gp, K, dtype):
     out = topk_case(marca, B, H, G, N, n_gp, K, dtype, seed=B * 100 + N)
     check_topk(*out, K)
