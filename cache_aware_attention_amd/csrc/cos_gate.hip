@@ -3,9 +3,10 @@
 // "LazyMAR" paper-notes page, Key designs (token cache): past the first three
 // layers, a token whose current feature is cosine-similar to the feature it
 // had when its cached value was computed skips recomputation.  Kernel 1
-// computes one cosine per token (a wave per token: 16-byte loads, float
-// accumulation of <x,y>, |x|^2, |y|^2, butterfly reduction) and the reuse
-// decision cos >= tau in float.  Kernel 2 (one workgroup per sequence) packs
+// computes one cosine per token (16-byte loads, float accumulation of <x,y>,
+// |x|^2, |y|^2 per lane, then a wave reduction) and the reuse decision
+// cos >= tau in float: several tokens per wave with all their loads in
+// flight for widths up to 256 pieces of 16 bytes, one token per wave above.  Kernel 2 (one workgroup per sequence) packs
 // the positions to recompute in ascending order with a block prefix sum.
 #include "device_util.h"
 #include "launch.h"
@@ -65,6 +66,73 @@ __global__ __launch_bounds__(kThreads) void cosine_kernel(const V* __restrict__ 
     }
 }
 
+// Several tokens per wave: kTPW tokens, kPPL 16-byte pieces per lane per
+// vector (pieces = W / elements-per-piece <= 64 * kPPL).  All loads of the
+// wave's tokens are issued before any arithmetic, so a wave keeps
+// 2 * kTPW * kPPL loads in flight; reductions stay in registers (DPP and
+// row swaps).  A token past the end reads the last token and is not stored.
+template <typename V, int kTPW, int kPPL>
+__global__ __launch_bounds__(kThreads) void cosine_multi_kernel(
+    const V* __restrict__ x, const V* __restrict__ y, float* __restrict__ cos_out,
+    uint8_t* __restrict__ reuse, long long tokens, int pieces, float tau, float eps) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long t0 =
+        ((long long)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave) * kTPW;
+    if (t0 >= tokens) return;  // wave-uniform
+    V xa[kTPW][kPPL], ya[kTPW][kPPL];
+#pragma unroll
+    for (int k = 0; k < kTPW; ++k) {
+        const long long t = (t0 + k < tokens) ? t0 + k : tokens - 1;
+        const V* xr = x + (size_t)t * pieces;
+        const V* yr = y + (size_t)t * pieces;
+#pragma unroll
+        for (int i = 0; i < kPPL; ++i) {
+            const int p = lane + kWave * i;
+            const int pc = (p < pieces) ? p : 0;  // lanes past the row reload piece 0 (unused)
+            xa[k][i] = xr[pc];
+            ya[k][i] = yr[pc];
+        }
+    }
+    float xy[kTPW], xx[kTPW], yy[kTPW];
+#pragma unroll
+    for (int k = 0; k < kTPW; ++k) {
+        xy[k] = 0.f;
+        xx[k] = 0.f;
+        yy[k] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kPPL; ++i)
+            if (lane + kWave * i < pieces) acc_piece(xa[k][i], ya[k][i], xy[k], xx[k], yy[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kTPW; ++k) {
+        const float sxy = wave_sum_dpp(xy[k]);
+        const float sxx = wave_sum_dpp(xx[k]);
+        const float syy = wave_sum_dpp(yy[k]);
+        if (lane == k && t0 + k < tokens) {
+            const float den = fmaxf(sqrtf(sxx) * sqrtf(syy), eps);
+            const float c = sxy / den;
+            cos_out[t0 + k] = c;
+            reuse[t0 + k] = (c >= tau) ? 1 : 0;
+        }
+    }
+}
+
+template <typename V, int kTPW>
+void launch_cosine_multi(const void* x, const void* y, float* cos_out, uint8_t* reuse,
+                         long long tokens, int pieces, float tau, float eps, hipStream_t stream) {
+    const long long waves = (tokens + kTPW - 1) / kTPW;
+    const long long blocks = (waves + kThreads / kWave - 1) / (kThreads / kWave);
+    const V* xv = static_cast<const V*>(x);
+    const V* yv = static_cast<const V*>(y);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    switch ((pieces + kWave - 1) / kWave) {
+        case 1: hipLaunchKernelGGL((cosine_multi_kernel<V, kTPW, 1>), grid, block, 0, stream, xv, yv, cos_out, reuse, tokens, pieces, tau, eps); break;
+        case 2: hipLaunchKernelGGL((cosine_multi_kernel<V, kTPW, 2>), grid, block, 0, stream, xv, yv, cos_out, reuse, tokens, pieces, tau, eps); break;
+        case 3: hipLaunchKernelGGL((cosine_multi_kernel<V, kTPW, 3>), grid, block, 0, stream, xv, yv, cos_out, reuse, tokens, pieces, tau, eps); break;
+        default: hipLaunchKernelGGL((cosine_multi_kernel<V, kTPW, 4>), grid, block, 0, stream, xv, yv, cos_out, reuse, tokens, pieces, tau, eps); break;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void compact_kernel(const uint8_t* __restrict__ reuse,
                                                            int32_t* __restrict__ compute_idx,
                                                            int32_t* __restrict__ compute_len,
@@ -96,7 +164,15 @@ int launch_cos_gate(const void* x_cur, const void* x_cached, float tau, float ep
     const long long tokens = (long long)B * N;
     const int waves_per_block = kThreads / kWave;
     const long long blocks = (tokens + waves_per_block - 1) / waves_per_block;
-    if (dtype == MAR_BF16) {
+    const int pieces = (dtype == MAR_BF16) ? W / 8 : W / 4;  // 16-byte pieces per token
+    if (pieces <= 4 * kWave) {
+        if (dtype == MAR_BF16)
+            launch_cosine_multi<uint4, 4>(x_cur, x_cached, cos_out, reuse_mask, tokens, pieces,
+                                          tau, eps, stream);
+        else
+            launch_cosine_multi<float4, 2>(x_cur, x_cached, cos_out, reuse_mask, tokens, pieces,
+                                           tau, eps, stream);
+    } else if (dtype == MAR_BF16) {
         hipLaunchKernelGGL(cosine_kernel<uint4>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                            static_cast<const uint4*>(x_cur), static_cast<const uint4*>(x_cached),
                            cos_out, reuse_mask, tokens, W / 8, tau, eps);

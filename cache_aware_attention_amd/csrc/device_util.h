@@ -43,6 +43,27 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Register-only wave reduction: DPP steps within 16-lane rows (quad xor 1,
+// quad xor 2, half-row mirror, row mirror), then gfx950's row swaps
+// (permlane16 / permlane32).  Every lane ends with the same bits, and the
+// combination order is fixed.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_mov<0xb1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4e>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);  // row_half_mirror
+    v += dpp_mov<0x140>(v);  // row_mirror
+    const uint32_t u = __float_as_uint(v);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t w = __float_as_uint(v);
+    auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Exclusive prefix sum of one int per thread over a block of kThreads
 // threads (multiple of 64).  `scratch` holds kThreads/64 ints of LDS.
 // Returns the exclusive prefix; *total receives the block sum.

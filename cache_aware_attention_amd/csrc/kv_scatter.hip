@@ -16,6 +16,8 @@
 namespace marca {
 namespace {
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 // Threads = B * M * H * pieces (pieces = row_bytes / 16), K and V in the same
 // thread.  Index order: piece fastest, then h, then m, then b.
 __global__ __launch_bounds__(256) void scatter_rows_kernel(
@@ -37,8 +39,12 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
     }
     const size_t src = (((size_t)b * H + h) * M + m) * pieces + piece;
     const size_t dst = (((size_t)b * H + h) * N + j) * pieces + piece;
-    k_cache[dst] = k_new[src];
-    v_cache[dst] = v_new[src];
+    // Nontemporal stores: the rows are read again only at a later step, and
+    // streaming them out now keeps their write-back out of the next kernel.
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, k_new[src]),
+                                reinterpret_cast<u32x4_t*>(k_cache + dst));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v_new[src]),
+                                reinterpret_cast<u32x4_t*>(v_cache + dst));
 }
 
 // Full rewrite: grid-stride copy of n16 16-byte pieces of both tensors, four
