@@ -105,9 +105,9 @@ __global__ __launch_bounds__(kThreads) void cosine_multi_kernel(
     }
 #pragma unroll
     for (int k = 0; k < kTPW; ++k) {
-        const float sxy = wave_sum_dpp(xy[k]);
-        const float sxx = wave_sum_dpp(xx[k]);
-        const float syy = wave_sum_dpp(yy[k]);
+        const float sxy = wave_sum(xy[k]);
+        const float sxx = wave_sum(xx[k]);
+        const float syy = wave_sum(yy[k]);
         if (lane == k && t0 + k < tokens) {
             const float den = fmaxf(sqrtf(sxx) * sqrtf(syy), eps);
             const float c = sxy / den;

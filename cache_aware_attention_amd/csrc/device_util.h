@@ -30,38 +30,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
-// Butterfly reductions over the 64 lanes of a wave; every lane gets the
-// result and the combination order is fixed, so results are deterministic.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
-
-// Register-only wave reduction: DPP steps within 16-lane rows (quad xor 1,
-// quad xor 2, half-row mirror, row mirror), then gfx950's row swaps
-// (permlane16 / permlane32).  Every lane ends with the same bits, and the
-// combination order is fixed.
+// Reductions over the 64 lanes of a wave, register-only: DPP steps within
+// 16-lane rows (quad xor 1, quad xor 2, half-row mirror, row mirror), then
+// gfx950's row swaps (permlane16 / permlane32).  Every lane ends with the
+// same bits, and the combination order is fixed, so results are
+// deterministic.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_mov(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-    v += dpp_mov<0xb1>(v);   // quad_perm [1,0,3,2]
-    v += dpp_mov<0x4e>(v);   // quad_perm [2,3,0,1]
-    v += dpp_mov<0x141>(v);  // row_half_mirror
-    v += dpp_mov<0x140>(v);  // row_mirror
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+    v = op(v, dpp_mov<0xb1>(v));   // quad_perm [1,0,3,2]
+    v = op(v, dpp_mov<0x4e>(v));   // quad_perm [2,3,0,1]
+    v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
+    v = op(v, dpp_mov<0x140>(v));  // row_mirror
     const uint32_t u = __float_as_uint(v);
     auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const uint32_t w = __float_as_uint(v);
     auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+    return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    return wave_reduce(v, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ float wave_max(float v) {
+    return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // Exclusive prefix sum of one int per thread over a block of kThreads

@@ -17,8 +17,9 @@
 // plain FMA version.
 // Kernel 2 (one workgroup per sequence): sums the partials over heads in a
 // fixed order (no float atomics, deterministic), ranks the eligible tokens by
-// counting larger 64-bit keys (orderable score << 32 | ~index, so equal
-// scores put the lower index first), emits the refreshing tokens, and
+// counting larger 64-bit keys with wave ballots (orderable score << 32 |
+// ~index, so equal scores put the lower index first), emits the refreshing
+// tokens, and
 // compacts the ascending cached complement with a block prefix sum.
 #include "device_util.h"
 #include "launch.h"
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void refresh_scores_lds_kernel(
     const uint16_t* __restrict__ q_gen, const uint16_t* __restrict__ k_full,
     float* __restrict__ ws, int G, int N, int NS, float scale_log2) {
     constexpr int kWaves = kThreads / kWave;
-    constexpr int kBatch = 4;  // key tiles whose loads a wave issues together
+    constexpr int kBatch = 8;  // key tiles whose loads a wave issues together
     extern __shared__ float s_lds[];  // [QT * 16][NS]
     __shared__ float stat_m[QT * 16], stat_inv[QT * 16];
     const int tid = threadIdx.x;
@@ -316,10 +317,12 @@ __device__ __forceinline__ uint64_t rank_key(float s, int j) {
 // Kernel 2.  The rank of an eligible token is the number of eligible tokens
 // whose 64-bit key is larger; keys are unique (the index is part of the key),
 // so ranks are a permutation and the K smallest ranks are the refreshing
-// tokens in (score descending, index ascending) order.  Each thread ranks
-// kPerThread tokens against every key held in LDS.
-constexpr int kPerThread = 4;
-__global__ __launch_bounds__(kThreads) void refresh_select_kernel(
+// tokens in (score descending, index ascending) order.  Each wave ranks
+// tokens w, w + kSelWaves, ...; lane l holds keys l, l + 64, ... and one
+// ballot per 64 keys counts the larger ones.
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / kWave;
+__global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ gp_idx, int ld_gp, int n_gp, int K,
     float inv_hg, float* __restrict__ scores, int32_t* __restrict__ active_idx, int ld_act,
     int32_t* __restrict__ cached_idx, int ld_cached, int32_t* __restrict__ cached_len, int H,
@@ -327,67 +330,96 @@ __global__ __launch_bounds__(kThreads) void refresh_select_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     uint64_t* keys = reinterpret_cast<uint64_t*>(smem);   // [N], 0 = not eligible
     uint8_t* state = smem + (size_t)N * sizeof(uint64_t);  // [N]: 0 cand, 1 G/P, 2 refresh
-    __shared__ int scan_scratch[kThreads / kWave];
+    __shared__ int scan_scratch[kSelWaves];
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
     const int b = blockIdx.x;
     int32_t* arow = active_idx + (size_t)b * ld_act;
 
-    for (int j = tid; j < N; j += kThreads) state[j] = 0;
-    for (int r = tid; r < K; r += kThreads) arow[n_gp + r] = -1;  // fewer eligible than K
+    // Both global reads (the G/P list and the head partials of this thread's
+    // first token) are issued before the first barrier so their latencies
+    // overlap.
+    const int gp0 = (tid < n_gp) ? gp_idx[(size_t)b * ld_gp + tid] : -1;
+    float s0 = 0.f;
+    if (tid < N)
+        for (int h = 0; h < H; ++h) s0 += ws[((size_t)b * H + h) * N + tid];  // fixed order
+    for (int j = tid; j < N; j += kSelThreads) state[j] = 0;
+    for (int r = tid; r < K; r += kSelThreads) arow[n_gp + r] = -1;  // fewer eligible than K
     __syncthreads();
-    for (int m = tid; m < n_gp; m += kThreads) {
-        const int j = gp_idx[(size_t)b * ld_gp + m];
+    for (int m = tid; m < n_gp; m += kSelThreads) {
+        const int j = (m == tid) ? gp0 : gp_idx[(size_t)b * ld_gp + m];
         arow[m] = j;
         if (j >= 0 && j < N) state[j] = 1;
     }
     __syncthreads();
-    for (int j = tid; j < N; j += kThreads) {
-        float s = 0.f;
-        for (int h = 0; h < H; ++h) s += ws[((size_t)b * H + h) * N + j];
+    for (int j = tid; j < N; j += kSelThreads) {
+        float s = s0;
+        if (j != tid) {
+            s = 0.f;
+            for (int h = 0; h < H; ++h) s += ws[((size_t)b * H + h) * N + j];
+        }
         s *= inv_hg;
         scores[(size_t)b * N + j] = s;
         keys[j] = (state[j] == 0) ? rank_key(s, j) : 0ull;
     }
     __syncthreads();
 
-    for (int j0 = tid * kPerThread; j0 < N; j0 += kThreads * kPerThread) {
-        uint64_t mine[kPerThread];
-        int rank[kPerThread];
+    // The first kRegs * 64 keys live in registers; keys past them (N > 512)
+    // are read from LDS in the counting loop.
+    constexpr int kRegs = 8;
+    uint64_t kr[kRegs];
 #pragma unroll
-        for (int e = 0; e < kPerThread; ++e) {
-            mine[e] = (j0 + e < N) ? keys[j0 + e] : 0ull;
-            rank[e] = 0;
-        }
-        for (int i = 0; i < N; ++i) {
-            const uint64_t other = keys[i];
+    for (int k = 0; k < kRegs; ++k) {
+        const int i = lane + kWave * k;
+        kr[k] = (i < N) ? keys[i] : 0ull;  // 0 is never larger than an eligible key
+    }
+    const int nblk = (N + kWave - 1) / kWave;
+    // The wave's tokens j = w + kSelWaves * (64 t + l): lane l fetches the key
+    // of its token for round t, and the round then walks the 64 tokens with
+    // the key taken from that lane (readlane), so no LDS access sits in the
+    // inner loop.
+    for (int t0 = w; t0 < N; t0 += kSelWaves * kWave) {
+        const int jl = t0 + kSelWaves * lane;
+        const uint64_t kl = (jl < N) ? keys[jl] : 0ull;
+        const int nt = min(kWave, (N - t0 + kSelWaves - 1) / kSelWaves);
+        for (int e = 0; e < nt; ++e) {
+            const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(kl), e);
+            const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(kl >> 32), e);
+            const uint64_t kj = (static_cast<uint64_t>(hi) << 32) | lo;
+            if (kj == 0) continue;  // not eligible (wave-uniform)
+            int cnt = 0;
 #pragma unroll
-            for (int e = 0; e < kPerThread; ++e) rank[e] += (other > mine[e]) ? 1 : 0;
-        }
-#pragma unroll
-        for (int e = 0; e < kPerThread; ++e) {
-            if (mine[e] != 0 && rank[e] < K) {
-                arow[n_gp + rank[e]] = j0 + e;
-                state[j0 + e] = 2;
+            for (int k = 0; k < kRegs; ++k)
+                if (k < nblk) cnt += __popcll(__ballot(kr[k] > kj));
+            for (int i0 = kRegs * kWave; i0 < N; i0 += kWave) {
+                const int i = i0 + lane;
+                cnt += __popcll(__ballot(i < N && keys[i] > kj));
+            }
+            if (cnt < K && lane == 0) {
+                const int j = t0 + kSelWaves * e;
+                arow[n_gp + cnt] = j;
+                state[j] = 2;
             }
         }
     }
     __syncthreads();
 
     // Ascending compaction of the remaining candidates (state 0).
-    const int per = (N + kThreads - 1) / kThreads;
+    const int per = (N + kSelThreads - 1) / kSelThreads;
     const int j0 = tid * per;
     const int j1 = min(N, j0 + per);
     int cnt = 0;
     for (int j = j0; j < j1; ++j) cnt += (state[j] == 0);
     int total = 0;
-    int pos = block_exclusive_scan<kThreads>(cnt, scan_scratch, &total);
+    int pos = block_exclusive_scan<kSelThreads>(cnt, scan_scratch, &total);
     int32_t* crow = cached_idx + (size_t)b * ld_cached;
     for (int j = j0; j < j1; ++j)
         if (state[j] == 0) {
             if (pos < ld_cached) crow[pos] = j;
             ++pos;
         }
-    for (int t = total + tid; t < ld_cached; t += kThreads) crow[t] = -1;
+    for (int t = total + tid; t < ld_cached; t += kSelThreads) crow[t] = -1;
     if (tid == 0) cached_len[b] = total;
 }
 
@@ -432,7 +464,7 @@ int launch_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp
     if (st != MAR_OK) return st;
     const size_t lds2 = (size_t)N * sizeof(uint64_t) + (size_t)N;
     const float inv_hg = 1.f / (float)(H * G);
-    hipLaunchKernelGGL(refresh_select_kernel, dim3(B), dim3(kThreads), lds2, stream, workspace,
+    hipLaunchKernelGGL(refresh_select_kernel, dim3(B), dim3(kSelThreads), lds2, stream, workspace,
                        gp_idx, ld_gp, n_gp, K, inv_hg, scores, active_idx, ld_act, cached_idx,
                        ld_cached, cached_len, H, N);
     return status_from_launch();
