@@ -154,6 +154,38 @@ def test_full_attention_case_and_single_query(marca):
         check(np64(out)[0], np64(lse)[0], ref_o, ref_l, dtype)
 
 
+@pytest.mark.parametrize("N", [128, 129, 200, 320])
+def test_full_attention_layers(marca, N):
+    """A == N, Nc == 0 with many queries: the workgroup kernel that shares each
+    unit's K/V across its query blocks (ragged last block and last chunk)."""
+    cfg = small_cfg("bf16", B=2, H=3, N=N, A=N, stale=False, seed=40 + N)
+    x = attention_inputs(cfg, DEV)
+    out, lse = run(marca, x, Nc=0, cached=None)
+    units = [(0, 0), (1, 2), (0, 1)]
+    ref_o, ref_l = oracle_units({**x, "cached": torch.zeros((1, 1), dtype=torch.int32)}, units, 0)
+    got_o = np.stack([np64(out[b, h]) for b, h in units])
+    got_l = np.stack([np64(lse[b, h]) for b, h in units])
+    check(got_o, got_l, ref_o, ref_l, "bf16")
+
+
+def test_full_attention_mar_l_layer(marca):
+    """A full-attention layer at the MAR-L shape (128 sequences, 16 heads, N = 320)."""
+    from mar_workloads import device_normal
+    B, H, N = 128, 16, 320
+    q = device_normal((B, H, N, 64), 301, DEV, torch.bfloat16)
+    k = device_normal((B, H, N, 64), 302, DEV, torch.bfloat16)
+    v = device_normal((B, H, N, 64), 303, DEV, torch.bfloat16)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    out = marca.mar_cache_attn_fwd(q, k, v, k, v, None, Nc=0, lse=lse)
+    torch.cuda.synchronize()
+    import oracle
+    for b, h in ((0, 0), (127, 15), (64, 7)):
+        sl = lambda t: np64(t[b:b + 1, h:h + 1])
+        o, l = oracle.cache_attention(sl(q), sl(k), sl(v), sl(k), sl(v),
+                                      np.zeros((1, 1), np.int32), 0.125, Nc=0)
+        check(np64(out[b, h])[None], np64(lse[b, h])[None], o[0], l[0], "bf16")
+
+
 @pytest.mark.parametrize("name", ["mar_b", "mar_l", "mar_h", "highres"])
 def test_full_size_sampled_units(marca, name):
     """Full-size MAR shapes, the launch configuration the benchmark times;
