@@ -154,6 +154,27 @@ def test_full_attention_case_and_single_query(marca):
         check(np64(out)[0], np64(lse)[0], ref_o, ref_l, dtype)
 
 
+@pytest.mark.parametrize("A,Nc", [(40, 200), (24, 296), (100, 150)])
+def test_batch_of_256_units(marca, A, Nc):
+    """256 (sequence, head) units, including more queries than one wave takes."""
+    cfg = small_cfg("bf16", B=32, H=8, N=A + Nc, A=A, seed=60 + A)
+    x = attention_inputs(cfg, DEV)
+    out, lse = run(marca, x)
+    units = [(0, 0), (31, 7), (17, 3), (5, 6)]
+    ref_o, ref_l = oracle_units(x, units, Nc)
+    check(np.stack([np64(out[b, h]) for b, h in units]),
+          np.stack([np64(lse[b, h]) for b, h in units]), ref_o, ref_l, "bf16")
+    # the fused update must also write each unit's active rows exactly once
+    kc, vc = x["k_cache"].clone(), x["v_cache"].clone()
+    act = x["active"].to(torch.int32).contiguous()
+    out2 = marca.mar_cache_attn_fwd_update(x["q_a"], x["k_a"], x["v_a"], kc, vc, x["cached"], act)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+    ak = act.long()[:, None, :, None].expand(-1, 8, -1, 64)
+    assert torch.equal(torch.gather(kc, 2, ak), x["k_a"])
+    assert torch.equal(torch.gather(vc, 2, ak), x["v_a"])
+
+
 @pytest.mark.parametrize("N", [128, 129, 200, 320])
 def test_full_attention_layers(marca, N):
     """A == N, Nc == 0 with many queries: the workgroup kernel that shares each
