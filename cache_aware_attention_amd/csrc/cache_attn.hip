@@ -310,6 +310,13 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         const int r0 = c * kChunk;
         uint32_t valid = 0;
 #pragma unroll
+        for (int k = 0; k < 4; ++k) {  // V first: it is consumed first (into LDS)
+            bool ok;
+            const uint4* p = reinterpret_cast<const uint4*>(
+                row_ptr(r0 + 8 * k + (lane >> 3), A, Nc, cidx_s, va_u, vc_u, ok));
+            cr.v[k] = p[lane & 7];
+        }
+#pragma unroll
         for (int t = 0; t < 2; ++t) {
             bool ok;
             const uint4* p = reinterpret_cast<const uint4*>(
@@ -317,13 +324,6 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
             cr.k[t][0] = p[g];
             cr.k[t][1] = p[4 + g];
             valid |= static_cast<uint32_t>(__ballot(ok) & 0xffffull) << (16 * t);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            bool ok;
-            const uint4* p = reinterpret_cast<const uint4*>(
-                row_ptr(r0 + 8 * k + (lane >> 3), A, Nc, cidx_s, va_u, vc_u, ok));
-            cr.v[k] = p[lane & 7];
         }
         cr.valid = valid;
     };
@@ -498,7 +498,9 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     auto step = [&](int c, auto buf_tag) __attribute__((always_inline)) {
         constexpr int BI = decltype(buf_tag)::value;
         constexpr int BN = (BI + kPF) % (kPF + 1);
+        __builtin_amdgcn_s_setprio(3);  // requests first: they keep HBM busy
         issue(min(c + kPF, nchunks - 1), cr[BN]);
+        __builtin_amdgcn_s_setprio(0);
         compute(c, cr[BI]);
     };
     // Whole groups without guards (so the state at the loop back edge is the
