@@ -34,15 +34,18 @@ extern "C" const char* mar_status_string(int status) {
 
 extern "C" int mar_version(void) { return 100; }
 
+// ragged: A and Nc are per-sequence capacities, each at most N (one
+// sequence's active plus cached counts are its own business).
 static int check_cache_attn(const void* q_a, const void* k_a, const void* v_a,
                             const void* k_cache, const void* v_cache, const int32_t* cached_idx,
                             int ldc, const void* out, int B, int H, int N, int A, int Nc, int D,
-                            float scale, int dtype) {
+                            float scale, int dtype, bool ragged = false) {
     if (!q_a || !k_a || !v_a || !k_cache || !v_cache || !out) return MAR_E_NULL;
     if (Nc > 0 && !cached_idx) return MAR_E_NULL;
     if (elem_bytes(dtype) == 0) return MAR_E_DTYPE;
     if (B < 1 || H < 1 || N < 1 || A < 1 || D < 1 || Nc < 0) return MAR_E_SHAPE;
-    if ((long long)A + Nc > N || (Nc > 0 && ldc < Nc)) return MAR_E_SHAPE;
+    if (ragged ? (A > N || Nc > N) : ((long long)A + Nc > N)) return MAR_E_SHAPE;
+    if (Nc > 0 && ldc < Nc) return MAR_E_SHAPE;
     if (D != kHeadDim) return MAR_E_UNSUPPORTED;
     if (!(scale > 0.f) || scale > 3.0e38f) return MAR_E_RANGE;  // positive and finite
     if (!aligned16(q_a) || !aligned16(k_a) || !aligned16(v_a) || !aligned16(k_cache) ||
@@ -61,6 +64,21 @@ extern "C" int mar_cache_attn_fwd(const void* q_a, const void* k_a, const void* 
     if (st != MAR_OK) return st;
     return marca::launch_cache_attn(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
                                     B, H, N, A, Nc, scale, dtype, stream);
+}
+
+extern "C" int mar_cache_attn_fwd_ragged(const void* q_a, const void* k_a, const void* v_a,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* cached_idx, int ldc,
+                                         const int32_t* a_len, const int32_t* c_len, void* out,
+                                         float* lse, int B, int H, int N, int A, int Nc, int D,
+                                         float scale, int dtype, void* stream) {
+    if (!a_len || !c_len) return MAR_E_NULL;
+    const int st = check_cache_attn(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, B, H,
+                                    N, A, Nc, D, scale, dtype, true);
+    if (st != MAR_OK) return st;
+    return marca::launch_cache_attn_ragged(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc,
+                                           a_len, c_len, out, lse, B, H, N, A, Nc, scale, dtype,
+                                           stream);
 }
 
 extern "C" int mar_cache_attn_fwd_update(const void* q_a, const void* k_a, const void* v_a,

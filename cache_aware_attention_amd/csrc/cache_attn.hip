@@ -64,30 +64,34 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(
     const T* __restrict__ q_a, const T* __restrict__ k_a, const T* __restrict__ v_a,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ cached_idx, int ldc, T* __restrict__ out,
-    float* __restrict__ lse, int H, int N, int A, int Nc, float scale_log2) {
+    float* __restrict__ lse, int H, int N, int A, int Nc, float scale_log2,
+    const int32_t* __restrict__ a_len, const int32_t* __restrict__ c_len) {
     __shared__ float q_s[4][kD];
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     const int u = blockIdx.x;  // (b, h) unit
     const int b = u / H;
     const int i = blockIdx.y * 4 + wid;  // query of this wave
-    const bool has_query = i < A;
+    // A and Nc are the row strides / list capacities; per-sequence counts may be smaller.
+    const int An = (a_len != nullptr) ? min(max(a_len[b], 0), A) : A;
+    const int Ncn = (c_len != nullptr) ? min(max(c_len[b], 0), Nc) : Nc;
+    const bool has_query = i < An;
     q_s[wid][lane] = has_query ? load1(q_a, ((size_t)u * A + i) * kD + lane) * scale_log2
                                : 0.f;
     __syncthreads();
     if (!has_query) return;  // no block-wide barrier after this point
 
-    const int n_rows = A + Nc;
+    const int n_rows = An + Ncn;
     const int32_t* cidx = cached_idx + (size_t)b * ldc;
     float m = -INFINITY, l = 0.f, o = 0.f;
     for (int r0 = 0; r0 < n_rows; r0 += kWave) {
         const int r = r0 + lane;
         long long off_k = -1, off_v = -1;
-        if (r < A) {
+        if (r < An) {
             off_k = ((long long)u * A + r) * kD;
             off_v = off_k;
         } else if (r < n_rows) {
-            const int n = cidx[r - A];
+            const int n = cidx[r - An];
             if (n >= 0 && n < N) {
                 off_k = ((long long)u * N + n) * kD + (1ll << 62);  // tag: cache source
                 off_v = off_k;
@@ -245,7 +249,8 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
                       uint16_t* __restrict__ out, float* __restrict__ lse, int units, int H,
                       int N, int A, int Nc, int n_groups, float scale_log2,
                       const int32_t* __restrict__ active_idx, int ld_act,
-                      int32_t* __restrict__ err_count) {
+                      int32_t* __restrict__ err_count, const int32_t* __restrict__ a_len,
+                      const int32_t* __restrict__ c_len) {
     constexpr int kPF = prefetch_depth(NQT);
     static_assert(kPF >= 1 && kPF <= 3, "prefetch depth");
     constexpr int kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
@@ -273,14 +278,19 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         if (u >= units) return;  // uniform over the (one-wave) workgroup
     }
     const int b = u / H;
+    // A and Nc are the row stride of q_a/k_a/v_a/out and the list capacity;
+    // with per-sequence lengths the unit's counts An <= A, Ncn <= Nc.
+    const int An = (a_len != nullptr) ? min(max(a_len[b], 0), A) : A;
+    const int Ncn = (c_len != nullptr) ? min(max(c_len[b], 0), Nc) : Nc;
     const int q0 = qg * kQueriesPerGroup;
-    const int nq = min(A - q0, 16 * NQT);  // queries of this group (>= 1)
+    if (q0 >= An) return;  // no queries in this group (uniform; before any barrier)
+    const int nq = min(An - q0, 16 * NQT);  // queries of this group (>= 1)
 
     const uint16_t* ka_u = k_a + static_cast<size_t>(u) * A * kD;
     const uint16_t* va_u = v_a + static_cast<size_t>(u) * A * kD;
     const uint16_t* kc_u = k_cache + static_cast<size_t>(u) * N * kD;
     const uint16_t* vc_u = v_cache + static_cast<size_t>(u) * N * kD;
-    const int T = A + Nc;
+    const int T = An + Ncn;
     const int nchunks = (T + kChunk - 1) / kChunk;
 
     // The first entries of the cached list are requested first: they gate
@@ -291,7 +301,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 #pragma unroll
     for (int k = 0; k < kIdxRegs; ++k) {
         const int c = lane + kWave * k;
-        iv[k] = (c < Nc) ? cidx_g[c] : -1;
+        iv[k] = (c < Ncn) ? cidx_g[c] : -1;
     }
 
     // Q tile as the B operand of S^T = K Q^T: lane holds query m16 of tile qt,
@@ -313,14 +323,14 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         for (int k = 0; k < 4; ++k) {  // V first: it is consumed first (into LDS)
             bool ok;
             const uint4* p = reinterpret_cast<const uint4*>(
-                row_ptr(r0 + 8 * k + (lane >> 3), A, Nc, cidx_s, va_u, vc_u, ok));
+                row_ptr(r0 + 8 * k + (lane >> 3), An, Ncn, cidx_s, va_u, vc_u, ok));
             cr.v[k] = p[lane & 7];
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             bool ok;
             const uint4* p = reinterpret_cast<const uint4*>(
-                row_ptr(r0 + 16 * t + m16, A, Nc, cidx_s, ka_u, kc_u, ok));
+                row_ptr(r0 + 16 * t + m16, An, Ncn, cidx_s, ka_u, kc_u, ok));
             cr.k[t][0] = p[g];
             cr.k[t][1] = p[4 + g];
             valid |= static_cast<uint32_t>(__ballot(ok) & 0xffffull) << (16 * t);
@@ -333,9 +343,9 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 #pragma unroll
         for (int k = 0; k < kIdxRegs; ++k) {
             const int c = lane + kWave * k;
-            if (c < Nc) cidx_s[c] = (iv[k] >= 0 && iv[k] < N) ? iv[k] : -1;
+            if (c < Ncn) cidx_s[c] = (iv[k] >= 0 && iv[k] < N) ? iv[k] : -1;
         }
-        for (int c = lane + kWave * kIdxRegs; c < Nc; c += kWave) {
+        for (int c = lane + kWave * kIdxRegs; c < Ncn; c += kWave) {
             const int n = cidx_g[c];
             cidx_s[c] = (n >= 0 && n < N) ? n : -1;
         }
@@ -343,7 +353,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
             // Only the first query group of a unit writes its rows.  An entry
             // outside [0, N) is skipped and, once per sequence, counted.
             const int32_t* ag = active_idx + static_cast<size_t>(b) * ld_act;
-            for (int r = lane; r < A; r += kWave) {
+            for (int r = lane; r < An; r += kWave) {
                 const int n = ag[r];
                 const bool ok = n >= 0 && n < N;
                 aidx_s[r] = (ok && qg == 0) ? n : -1;
@@ -358,7 +368,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     // When the sequence has fewer than kPF chunks the spare buffers load its
     // last chunk again (never used), so every path issues the same loads.
     ChunkRegs cr[kPF + 1];
-    if (A >= kChunk) {
+    if (An >= kChunk) {
         issue(0, cr[0]);
         stage_list();
     } else {
@@ -399,7 +409,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         for (int k = 0; k < 4; ++k)
             *reinterpret_cast<uint4*>(tile + vst + 1024 * k) = ch.v[k];
         if constexpr (UPDATE) {
-            if (c * kChunk < A) {  // wave-uniform: the chunk holds active rows
+            if (c * kChunk < An) {  // wave-uniform: the chunk holds active rows
                 // Buffer stores: an offset past the unit's N rows (inactive
                 // lane, skipped entry) is dropped by the range check.
                 constexpr uint32_t kSkip = 0x80000000u;
@@ -411,7 +421,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int r = c * kChunk + 16 * t + m16;
-                    const int n = (r < A) ? aidx_s[r] : -1;
+                    const int n = (r < An) ? aidx_s[r] : -1;
                     const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.k[t][0]),
                                                            rk, off + 16 * g, 0, kNT);
@@ -421,7 +431,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int r = c * kChunk + 8 * k + (lane >> 3);
-                    const int n = (r < A) ? aidx_s[r] : -1;
+                    const int n = (r < An) ? aidx_s[r] : -1;
                     const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.v[k]),
                                                            rv, off + 16 * (lane & 7), 0, kNT);
@@ -554,7 +564,8 @@ int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
                 const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* cached_idx,
                 int ldc, uint16_t* out, float* lse, int B, int H, int N, int A, int Nc,
                 int n_groups, float scale_log2, const int32_t* active_idx, int ld_act,
-                int32_t* err_count, hipStream_t stream) {
+                int32_t* err_count, const int32_t* a_len, const int32_t* c_len,
+                hipStream_t stream) {
     const int units = B * H;
     const int grid = (n_groups == 1) ? units : ((units + 7) / 8) * 8 * n_groups;
     constexpr size_t kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
@@ -562,7 +573,7 @@ int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
                        (UPDATE ? static_cast<size_t>(A) * 4 : 0);
     hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE>), dim3(grid), dim3(64), lds, stream, q_a,
                        k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse, units, H, N, A, Nc,
-                       n_groups, scale_log2, active_idx, ld_act, err_count);
+                       n_groups, scale_log2, active_idx, ld_act, err_count, a_len, c_len);
     return status_from_launch();
 }
 
@@ -570,35 +581,38 @@ template <bool UPDATE>
 int dispatch_mfma(const uint16_t* q, const uint16_t* ka, const uint16_t* va, const uint16_t* kc,
                   const uint16_t* vc, const int32_t* cached_idx, int ldc, uint16_t* o, float* lse,
                   int B, int H, int N, int A, int Nc, float scale_log2, const int32_t* active_idx,
-                  int ld_act, int32_t* err_count, hipStream_t stream) {
+                  int ld_act, int32_t* err_count, const int32_t* a_len, const int32_t* c_len,
+                  hipStream_t stream) {
     const int n_groups = (A + kQueriesPerGroup - 1) / kQueriesPerGroup;
     const int nqt = (n_groups > 1) ? 4 : (A + 15) / 16;
     switch (nqt) {
         case 1:
             return launch_mfma<1, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
                                           Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
-                                          stream);
+                                          a_len, c_len, stream);
         case 2:
             return launch_mfma<2, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
                                           Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
-                                          stream);
+                                          a_len, c_len, stream);
         case 3:
             return launch_mfma<3, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
                                           Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
-                                          stream);
+                                          a_len, c_len, stream);
         default:
             return launch_mfma<4, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
                                           Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
-                                          stream);
+                                          a_len, c_len, stream);
     }
 }
 
 }  // namespace
 
-int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a, const void* k_cache,
-                      const void* v_cache, const int32_t* cached_idx, int ldc, void* out,
-                      float* lse, int B, int H, int N, int A, int Nc, float scale, int dtype,
-                      void* stream_v) {
+namespace {
+
+int launch_attn_impl(const void* q_a, const void* k_a, const void* v_a, const void* k_cache,
+                     const void* v_cache, const int32_t* cached_idx, int ldc, void* out,
+                     float* lse, int B, int H, int N, int A, int Nc, float scale, int dtype,
+                     const int32_t* a_len, const int32_t* c_len, void* stream_v) {
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
     const float scale_log2 = scale * kLog2e;
     if (cached_idx == nullptr) ldc = 0;  // only legal with Nc == 0: never dereferenced
@@ -610,7 +624,7 @@ int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a, const v
         const uint16_t* vc = static_cast<const uint16_t*>(v_cache);
         uint16_t* o = static_cast<uint16_t*>(out);
         return dispatch_mfma<false>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A, Nc,
-                                    scale_log2, nullptr, 0, nullptr, stream);
+                                    scale_log2, nullptr, 0, nullptr, a_len, c_len, stream);
     }
     const dim3 grid(B * H, (A + 3) / 4);
     if (dtype == MAR_BF16) {
@@ -618,15 +632,35 @@ int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a, const v
                            static_cast<const uint16_t*>(q_a), static_cast<const uint16_t*>(k_a),
                            static_cast<const uint16_t*>(v_a), static_cast<const uint16_t*>(k_cache),
                            static_cast<const uint16_t*>(v_cache), cached_idx, ldc,
-                           static_cast<uint16_t*>(out), lse, H, N, A, Nc, scale_log2);
+                           static_cast<uint16_t*>(out), lse, H, N, A, Nc, scale_log2, a_len,
+                           c_len);
     } else {
         hipLaunchKernelGGL(attn_rowwise_kernel<float>, grid, dim3(256), 0, stream,
                            static_cast<const float*>(q_a), static_cast<const float*>(k_a),
                            static_cast<const float*>(v_a), static_cast<const float*>(k_cache),
                            static_cast<const float*>(v_cache), cached_idx, ldc,
-                           static_cast<float*>(out), lse, H, N, A, Nc, scale_log2);
+                           static_cast<float*>(out), lse, H, N, A, Nc, scale_log2, a_len, c_len);
     }
     return status_from_launch();
+}
+
+}  // namespace
+
+int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a, const void* k_cache,
+                      const void* v_cache, const int32_t* cached_idx, int ldc, void* out,
+                      float* lse, int B, int H, int N, int A, int Nc, float scale, int dtype,
+                      void* stream_v) {
+    return launch_attn_impl(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse, B, H, N,
+                            A, Nc, scale, dtype, nullptr, nullptr, stream_v);
+}
+
+int launch_cache_attn_ragged(const void* q_a, const void* k_a, const void* v_a,
+                             const void* k_cache, const void* v_cache, const int32_t* cached_idx,
+                             int ldc, const int32_t* a_len, const int32_t* c_len, void* out,
+                             float* lse, int B, int H, int N, int A, int Nc, float scale,
+                             int dtype, void* stream_v) {
+    return launch_attn_impl(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse, B, H, N,
+                            A, Nc, scale, dtype, a_len, c_len, stream_v);
 }
 
 int launch_cache_attn_update(const void* q_a, const void* k_a, const void* v_a, void* k_cache,
@@ -640,7 +674,7 @@ int launch_cache_attn_update(const void* q_a, const void* k_a, const void* v_a, 
             static_cast<const uint16_t*>(q_a), static_cast<const uint16_t*>(k_a),
             static_cast<const uint16_t*>(v_a), static_cast<const uint16_t*>(k_cache),
             static_cast<const uint16_t*>(v_cache), cached_idx, ldc, static_cast<uint16_t*>(out),
-            lse, B, H, N, A, Nc, scale * kLog2e, active_idx, ld_act, err_count,
+            lse, B, H, N, A, Nc, scale * kLog2e, active_idx, ld_act, err_count, nullptr, nullptr,
             static_cast<hipStream_t>(stream_v));
     }
     // Row-wise path: the attention, then the row scatter on the same stream

@@ -14,6 +14,12 @@ int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a,
                       int B, int H, int N, int A, int Nc, float scale, int dtype,
                       void* stream);
 
+int launch_cache_attn_ragged(const void* q_a, const void* k_a, const void* v_a,
+                             const void* k_cache, const void* v_cache, const int32_t* cached_idx,
+                             int ldc, const int32_t* a_len, const int32_t* c_len, void* out,
+                             float* lse, int B, int H, int N, int A, int Nc, float scale,
+                             int dtype, void* stream);
+
 int launch_cache_attn_update(const void* q_a, const void* k_a, const void* v_a, void* k_cache,
                              void* v_cache, const int32_t* cached_idx, int ldc,
                              const int32_t* active_idx, int ld_act, int32_t* err_count, void* out,

@@ -94,6 +94,30 @@ int mar_cache_attn_fwd(const void* q_a, const void* k_a, const void* v_a,
                        float scale, int dtype, void* stream);
 
 /*
+ * Cache-aware attention with per-sequence set sizes  ([LazyMAR] Key designs,
+ * token cache: each sequence recomputes only the tokens its gate selects, so
+ * the active and cached sets differ in size from sequence to sequence;
+ * [MARche] Key Design 2, Eq. 1-2, for the attention itself).
+ *
+ * As mar_cache_attn_fwd, with A and Nc read as capacities:
+ *   a_len [B] device int32: sequence b has An = min(max(a_len[b], 0), A)
+ *         active rows -- the first An rows of its q_a/k_a/v_a blocks;
+ *   c_len [B] device int32: its first min(max(c_len[b], 0), Nc) entries of
+ *         cached_idx are its cached set.
+ * Rows of out (and lse) at or past An are not written.  A sequence with An = 0
+ * computes nothing.  Requirements and errors as for mar_cache_attn_fwd,
+ * except that A <= N and Nc <= N replace A + Nc <= N (the capacities are
+ * maxima over sequences), plus a_len and c_len != NULL.
+ */
+int mar_cache_attn_fwd_ragged(const void* q_a, const void* k_a, const void* v_a,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* cached_idx, int ldc,
+                              const int32_t* a_len, const int32_t* c_len,
+                              void* out, float* lse,
+                              int B, int H, int N, int A, int Nc, int D,
+                              float scale, int dtype, void* stream);
+
+/*
  * Cache-aware attention fused with the cache update of the active rows
  * ([MARche] Overall Architecture: attention over the active and cached sets
  * as one fused operator; abstract on the Pith page: only the recomputed

@@ -91,6 +91,16 @@ def test_cache_attn_update_rejections(lib):
     assert attn_upd(lib, dtype=3) == E_DTYPE
 
 
+def test_cache_attn_ragged_rejections(lib):
+    f = lambda **kw: lib.mar_cache_attn_fwd_ragged(
+        kw.get("q", P), P, P, P, P, kw.get("cidx", P), kw.get("ldc", 272), kw.get("al", P),
+        kw.get("cl", P), P, None, 2, 2, 320, kw.get("A", 48), 272, 64, 0.125, 1, None)
+    assert f(al=None) == E_NULL and f(cl=None) == E_NULL
+    assert f(q=None) == E_NULL
+    assert f(A=321) == E_SHAPE     # a capacity larger than N
+    assert f(ldc=100) == E_SHAPE
+
+
 def test_scatter_rejections(lib):
     f = lib.mar_kv_scatter_refresh
     assert f(None, P, P, P, P, 48, None, 2, 2, 320, 48, 64, 1, None) == E_NULL
