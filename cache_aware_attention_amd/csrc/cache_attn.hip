@@ -241,7 +241,9 @@ struct ChunkRegs {
 // them for the attention.  The rows read from the caches are the cached set,
 // which is disjoint from the active positions, so the reads and the writes of
 // one unit never touch the same row and different units never share a row.
-template <int NQT, bool UPDATE>
+// RAGGED: per-sequence active / cached counts from a_len / c_len (a separate
+// instantiation, so the uniform-count kernel carries none of it).
+template <int NQT, bool UPDATE, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
                       const uint16_t* __restrict__ v_a, const uint16_t* k_cache,
@@ -280,10 +282,14 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     const int b = u / H;
     // A and Nc are the row stride of q_a/k_a/v_a/out and the list capacity;
     // with per-sequence lengths the unit's counts An <= A, Ncn <= Nc.
-    const int An = (a_len != nullptr) ? min(max(a_len[b], 0), A) : A;
-    const int Ncn = (c_len != nullptr) ? min(max(c_len[b], 0), Nc) : Nc;
+    int An = A, Ncn = Nc;
+    if constexpr (RAGGED) {
+        An = min(max(a_len[b], 0), A);
+        Ncn = min(max(c_len[b], 0), Nc);
+    }
     const int q0 = qg * kQueriesPerGroup;
-    if (q0 >= An) return;  // no queries in this group (uniform; before any barrier)
+    if constexpr (RAGGED)
+        if (q0 >= An) return;  // no queries in this group (uniform; before any barrier)
     const int nq = min(An - q0, 16 * NQT);  // queries of this group (>= 1)
 
     const uint16_t* ka_u = k_a + static_cast<size_t>(u) * A * kD;
@@ -571,9 +577,16 @@ int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
     constexpr size_t kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
     const size_t lds = kTileBytes + static_cast<size_t>(Nc > 0 ? Nc : 1) * 4 +
                        (UPDATE ? static_cast<size_t>(A) * 4 : 0);
-    hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE>), dim3(grid), dim3(64), lds, stream, q_a,
-                       k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse, units, H, N, A, Nc,
-                       n_groups, scale_log2, active_idx, ld_act, err_count, a_len, c_len);
+    if (a_len != nullptr)
+        hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, true>), dim3(grid), dim3(64), lds,
+                           stream, q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
+                           units, H, N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
+                           err_count, a_len, c_len);
+    else
+        hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, false>), dim3(grid), dim3(64), lds,
+                           stream, q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
+                           units, H, N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
+                           err_count, a_len, c_len);
     return status_from_launch();
 }
 
