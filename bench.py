@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 METRIC = "cache-aware attn active-query tok/s + HBM GB/s (% peak), MAR-L-like shape"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mar_l_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "cache_aware_attention_amd", "csrc", "cache_attn.hip")
 
@@ -164,6 +165,7 @@ def build_inputs(cfg, dev):
         "reuse": torch.empty((cfg.B, cfg.N), dtype=torch.uint8, device=dev),
         "cidx": torch.empty((cfg.B, cfg.N), dtype=torch.int32, device=dev),
         "clen": torch.empty((cfg.B,), dtype=torch.int32, device=dev),
+        "full_out": torch.empty((cfg.B, cfg.H, cfg.N, cfg.D), dtype=torch.bfloat16, device=dev),
     }
     torch.cuda.synchronize()
     return x
@@ -239,6 +241,14 @@ def main():
                                         L["v_cache"], x["cached_idx"], x["active_idx"],
                                         Nc=plan.n_cached, out=L["out"])
 
+    def full_attn(l):
+        """A full-attention layer (layers 1-2 of every step, every layer of a
+        refresh step): all N tokens active, no cached rows.  Layer l's stored
+        K/V stand in for its fresh K/V and the next layer's K for its Q."""
+        L, Lq = x["layers"][l], x["layers"][(l + 1) % n_ca]
+        marca.mar_cache_attn_fwd(Lq["k_cache"], L["k_cache"], L["v_cache"], L["k_cache"],
+                                 L["v_cache"], None, Nc=0, out=x["full_out"])
+
     def cfg_reuse():
         marca.mar_cfg_residual(x["cond"], residual=x["residual"], mode=marca.MAR_CFG_REUSE,
                                uncond_out=x["uncond_out"])
@@ -289,6 +299,7 @@ def main():
         span("attn_update", lambda: [fused(l, plan) for l in range(n_ca)], n_ca)
         span("cfg", cfg_reuse, 1)
         span("gate", gate, 1)
+        span("full_attn", lambda: [full_attn(l) for l in range(n_ca)], n_ca)
         return spans
 
     print("bench: warmup", file=sys.stderr, flush=True)
@@ -335,6 +346,10 @@ def main():
     bytes_fused = bytes_call + 2 * cfg.B * cfg.H * cfg.A * cfg.D * 2  # + K_A, V_A rows written
     achieved_fused = bytes_fused / (avg_us["attn_update"] * 1e-6) / 1e9
 
+    full_flops = 4 * cfg.B * cfg.H * cfg.N * cfg.N * cfg.D
+    full_tflops = full_flops / (avg_us["full_attn"] * 1e-6) / 1e12
+    full_bytes = 4 * cfg.B * cfg.H * cfg.N * cfg.D * 2
+
     copy_gbs = None
     try:  # achievable HBM: the plain full-refresh copy over one layer's caches
         L0, L1 = x["layers"][0], x["layers"][1]
@@ -377,6 +392,14 @@ def main():
             "roofline": {"bound": "hbm", "achieved": achieved_fused, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": achieved_fused / PEAK_HBM_GBS,
                          "bytes_per_call": bytes_fused}},
+        "full_attention": {
+            "what": "mar_cache_attn_fwd with A = N and no cached rows (layers 1-2 of every "
+                    "step, every layer of a refresh step), outside the step above",
+            "us_per_call": avg_us["full_attn"],
+            "roofline": {"bound": "mfma", "achieved": full_tflops, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": full_tflops / PEAK_BF16_TFLOPS,
+                         "flops_per_call": full_flops},
+            "gbs": full_bytes / (avg_us["full_attn"] * 1e-6) / 1e9},
         "attn_bytes_per_call": bytes_call,
         "attn_tok_per_s": cfg.B * cfg.A / (avg_us["attn"] * 1e-6),
         "copy_gbs": copy_gbs,

@@ -22,6 +22,10 @@ LIB = PKG / "libmarca.so"
 HIP_SOURCES = ["cache_attn.hip", "kv_scatter.hip", "refresh_topk.hip", "cos_gate.hip",
                "cfg_residual.hip"]
 CPP_SOURCES = ["abi.cpp", "schedule.cpp"]
+# Per-file device flags.  The attention kernels assume NaN-free inputs (a
+# documented precondition of the ABI), which lets the compiler take maxima of
+# matrix-core results without quieting them first.
+HIP_EXTRA_FLAGS = {"cache_attn.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 
@@ -55,7 +59,8 @@ def build(verbose: bool = False) -> Path:
     jobs = []
     for src in HIP_SOURCES:
         obj = BUILD / (src + ".o")
-        jobs.append([hipcc(), *hip_flags(), "-c", str(CSRC / src), "-o", str(obj)])
+        jobs.append([hipcc(), *hip_flags(), *HIP_EXTRA_FLAGS.get(src, []), "-c", str(CSRC / src),
+                     "-o", str(obj)])
     for src in CPP_SOURCES:
         obj = BUILD / (src + ".o")
         jobs.append(["g++", "-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra",

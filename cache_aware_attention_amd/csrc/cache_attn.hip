@@ -15,15 +15,20 @@
 //    query group of up to 64 queries.  S^T = K Q^T and O^T = V^T P^T run on
 //    v_mfma_f32_16x16x32_bf16; K goes straight from HBM into MFMA operand
 //    registers (each lane loads 16-byte pieces of one 128-byte key row), V is
-//    staged through LDS (padded rows) so each lane can read the 8 key rows of
-//    one d column it needs for the PV operand.  The next chunk's loads are
-//    issued before the current chunk is computed.  The unit's cached index
-//    list is staged in LDS once.
+//    staged through a swizzled LDS tile and read back with the transposing
+//    ds_read_b64_tr_b16 as the PV operand.  The next chunk's loads are issued
+//    before the current chunk is computed.  The unit's cached index list is
+//    staged in LDS once.  Separate instantiations serve per-sequence counts,
+//    the fused cache update, and the case with no cached rows (the
+//    full-attention layers), whose keys are contiguous rows read at fixed
+//    per-lane offsets.
 //  * attn_rowwise_kernel (fp32 any A, bf16 A < 16): one wave per query, one
 //    lane per head-dim element; plain FMA.  Exact-precision path for fp32.
 //
 // Head dim is fixed at 64 (MAR-B/L/H all use 64).  The cached index list is
-// sanitised: an entry outside [0, N) is skipped, never dereferenced.
+// sanitised: an entry outside [0, N) is skipped, never dereferenced.  Inputs
+// are NaN-free (a precondition of the ABI); this file is compiled with
+// -fno-honor-nans, so maxima of matrix-core results need no quieting step.
 #include <type_traits>
 
 #include "device_util.h"
@@ -243,7 +248,11 @@ struct ChunkRegs {
 // one unit never touch the same row and different units never share a row.
 // RAGGED: per-sequence active / cached counts from a_len / c_len (a separate
 // instantiation, so the uniform-count kernel carries none of it).
-template <int NQT, bool UPDATE, bool RAGGED>
+// DENSE: no cached rows (Nc == 0, the full-attention layers): the unit's keys
+// are rows 0..A-1 of k_a/v_a, read with range-checked buffer loads at
+// per-lane offsets fixed for the whole sequence.  A row past A reads as zero
+// and is masked like a missing row.
+template <int NQT, bool UPDATE, bool RAGGED, bool DENSE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
                       const uint16_t* __restrict__ v_a, const uint16_t* k_cache,
@@ -298,6 +307,13 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     const uint16_t* vc_u = v_cache + static_cast<size_t>(u) * N * kD;
     const int T = An + Ncn;
     const int nchunks = (T + kChunk - 1) / kChunk;
+    static_assert(!DENSE || (!UPDATE && !RAGGED), "dense rows: plain attention only");
+    const __amdgpu_buffer_rsrc_t rka = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(ka_u), 0, An * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rva = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(va_u), 0, An * kD * 2, 0x00020000);
+    const int k_lofs = m16 * (kD * 2) + 16 * g;                 // K: row m16, piece g
+    const int v_lofs = (lane >> 3) * (kD * 2) + 16 * (lane & 7);  // V: row lane/8, piece lane%8
 
     // The first entries of the cached list are requested first: they gate
     // every chunk that holds a cached row.
@@ -307,7 +323,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 #pragma unroll
     for (int k = 0; k < kIdxRegs; ++k) {
         const int c = lane + kWave * k;
-        iv[k] = (c < Ncn) ? cidx_g[c] : -1;
+        iv[k] = (!DENSE && c < Ncn) ? cidx_g[c] : -1;
     }
 
     // Q tile as the B operand of S^T = K Q^T: lane holds query m16 of tile qt,
@@ -324,6 +340,23 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 
     auto issue = [&](int c, ChunkRegs& cr) __attribute__((always_inline)) {
         const int r0 = c * kChunk;
+        if constexpr (DENSE) {
+            const int rb = r0 * (kD * 2);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                cr.v[k] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rva, rb + v_lofs + 1024 * k, 0, 0));
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                cr.k[t][0] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rka, rb + k_lofs + 2048 * t, 0, 0));
+                cr.k[t][1] = __builtin_bit_cast(
+                    uint4,
+                    __builtin_amdgcn_raw_buffer_load_b128(rka, rb + k_lofs + 2048 * t + 64, 0, 0));
+            }
+            cr.valid = 0;
+            return;
+        }
         uint32_t valid = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {  // V first: it is consumed first (into LDS)
@@ -346,6 +379,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 
     // Stage the cached list (entries outside [0, N) become -1).
     auto stage_list = [&]() __attribute__((always_inline)) {
+        if constexpr (DENSE) return;
 #pragma unroll
         for (int k = 0; k < kIdxRegs; ++k) {
             const int c = lane + kWave * k;
@@ -451,7 +485,8 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
             const uint2 hi = lds_tr_b64(tile + vofs[1][dt]);
             va[dt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
-        const bool full = ch.valid == 0xffffffffu;  // wave-uniform
+        // wave-uniform
+        const bool full = DENSE ? (c * kChunk + kChunk <= An) : ch.valid == 0xffffffffu;
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
             if (!tile_on[qt]) continue;  // wave-uniform
@@ -471,7 +506,9 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (!((ch.valid >> (16 * t + 4 * g + i)) & 1u)) s[t][i] = -INFINITY;
+                        if (DENSE ? (c * kChunk + 16 * t + 4 * g + i >= An)
+                                  : !((ch.valid >> (16 * t + 4 * g + i)) & 1u))
+                            s[t][i] = -INFINITY;
             }
             const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -577,13 +614,22 @@ int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
     constexpr size_t kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
     const size_t lds = kTileBytes + static_cast<size_t>(Nc > 0 ? Nc : 1) * 4 +
                        (UPDATE ? static_cast<size_t>(A) * 4 : 0);
+    if constexpr (!UPDATE) {
+        if (a_len == nullptr && Nc == 0) {
+            hipLaunchKernelGGL((attn_mfma_kernel<NQT, false, false, true>), dim3(grid), dim3(64),
+                               lds, stream, q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out,
+                               lse, units, H, N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
+                               err_count, a_len, c_len);
+            return status_from_launch();
+        }
+    }
     if (a_len != nullptr)
-        hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, true>), dim3(grid), dim3(64), lds,
+        hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, true, false>), dim3(grid), dim3(64), lds,
                            stream, q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
                            units, H, N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
                            err_count, a_len, c_len);
     else
-        hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, false>), dim3(grid), dim3(64), lds,
+        hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, false, false>), dim3(grid), dim3(64), lds,
                            stream, q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
                            units, H, N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
                            err_count, a_len, c_len);
