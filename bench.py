@@ -177,6 +177,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the whole-decode timing (for counter runs)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the plain copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -189,7 +191,7 @@ def main():
     import torch
 
     import cache_aware_attention_amd as marca
-    from mar_workloads import CONFIGS
+    from mar_workloads import CONFIGS, cosine_counts
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -213,6 +215,8 @@ def main():
     x = build_inputs(cfg, dev)
     counts = [cfg.n_gen] * (cfg.steps)
     counts[0] = 0
+    # the whole decode follows the cosine masking schedule over the 256 image tokens
+    decode_counts = cosine_counts(cfg.n_img, cfg.steps)
     step_t = 4  # a non-refresh step (4 % 3 != 0) with 16 previous + 16 generating tokens
     n_ca = cfg.layers - 2
 
@@ -282,6 +286,45 @@ def main():
         cfg_reuse()
         gate()
 
+    def full_refresh(l):
+        """A refresh step of cache-aware layer l: full attention over all N tokens
+        and the rewrite of every row of the layer's cache with the fresh K/V, in
+        one call (the next layer's stored K/V stand in for the fresh K/V, the one
+        after it for Q)."""
+        L, Ln, Lq = (x["layers"][(l + i) % n_ca] for i in range(3))
+        marca.mar_cache_attn_fwd_update(Lq["k_cache"], Ln["k_cache"], Ln["v_cache"],
+                                        L["k_cache"], L["v_cache"], None, None, Nc=0,
+                                        out=x["full_out"])
+
+    def decode(use_cache):
+        """A whole 64-step decode of the attention path.  With the cache: on a
+        refresh step (t mod 3 = 0) every layer runs full attention and rewrites
+        its cache, and the CFG residual is stored; on the other steps layers 1-2
+        run full attention and layers 3-32 run the cached step above.  Without
+        the cache every layer of every step runs full attention."""
+        for t in range(cfg.steps):
+            if not use_cache:
+                for l in range(cfg.layers):
+                    full_attn(l % n_ca)
+                continue
+            plan = marca.mar_plan_step(decode_counts, t, cfg.N, cfg.budget)
+            if plan.refresh:
+                full_attn(0)
+                full_attn(1)
+                for l in range(n_ca):
+                    full_refresh(l)
+                marca.mar_cfg_residual(x["cond"], x["uncond_out"], residual=x["residual"],
+                                       mode=marca.MAR_CFG_STORE)
+                continue
+            full_attn(0)
+            full_attn(1)
+            topk(plan)
+            for l in range(n_ca):
+                attn(l, plan)
+                scatter(l)
+            cfg_reuse()
+            gate()
+
     def timed_kernels():
         """The same launches as one step, grouped by kernel so that one pair of HIP
         events brackets each group of back-to-back launches (an event pair around
@@ -300,6 +343,7 @@ def main():
         span("cfg", cfg_reuse, 1)
         span("gate", gate, 1)
         span("full_attn", lambda: [full_attn(l) for l in range(n_ca)], n_ca)
+        span("full_refresh", lambda: [full_refresh(l) for l in range(n_ca)], n_ca)
         return spans
 
     print("bench: warmup", file=sys.stderr, flush=True)
@@ -331,6 +375,20 @@ def main():
     f1.record(stream)
     torch.cuda.synchronize()
     ms_per_step_fused = f0.elapsed_time(f1) / args.steps
+
+    # Timed region 1c: whole decodes, with and without the cache.
+    decode_ms = {}
+    for use_cache in (() if args.no_decode else (True, False)):
+        decode(use_cache)
+        torch.cuda.synchronize()
+        d0, d1 = ev(), ev()
+        d0.record(stream)
+        decode(use_cache)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        decode_ms[use_cache] = d0.elapsed_time(d1)
+    n_refresh_steps = sum(marca.mar_plan_step(decode_counts, t, cfg.N, cfg.budget).refresh
+                          for t in range(cfg.steps))
 
     # Timed region 2: the same launches, grouped per kernel, HIP events per group.
     groups = [timed_kernels() for _ in range(args.steps)]
@@ -396,10 +454,20 @@ def main():
             "what": "mar_cache_attn_fwd with A = N and no cached rows (layers 1-2 of every "
                     "step, every layer of a refresh step), outside the step above",
             "us_per_call": avg_us["full_attn"],
+            "refresh_us_per_call": avg_us["full_refresh"],
+            "refresh_what": "the same layer on a refresh step: mar_cache_attn_fwd_update with no "
+                            "active list (full attention and every cache row rewritten, one call)",
             "roofline": {"bound": "mfma", "achieved": full_tflops, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": full_tflops / PEAK_BF16_TFLOPS,
                          "flops_per_call": full_flops},
             "gbs": full_bytes / (avg_us["full_attn"] * 1e-6) / 1e9},
+        "decode": None if args.no_decode else {
+            "what": "one 64-step decode of the attention path (every layer's attention, cache "
+                    "writes, top-K, CFG and gate; no projections or MLPs), with the cache "
+                    "(refresh every 3rd step) and without it (full attention everywhere)",
+            "steps": cfg.steps, "refresh_steps": n_refresh_steps, "layers": cfg.layers,
+            "ms": decode_ms.get(True), "ms_no_cache": decode_ms.get(False),
+            "speedup": decode_ms.get(False, 0) / decode_ms.get(True, 1)},
         "attn_bytes_per_call": bytes_call,
         "attn_tok_per_s": cfg.B * cfg.A / (avg_us["attn"] * 1e-6),
         "copy_gbs": copy_gbs,

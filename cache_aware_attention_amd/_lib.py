@@ -196,7 +196,8 @@ def mar_cache_attn_fwd_ragged(q_a, k_a, v_a, k_cache, v_cache, cached_idx, a_len
 def mar_cache_attn_fwd_update(q_a, k_a, v_a, k_cache, v_cache, cached_idx, active_idx, Nc=None,
                               out=None, lse=None, err_count=None, scale=None, stream=None):
     """mar_cache_attn_fwd, plus k_cache/v_cache rows at active_idx [B, ld] (first A
-    entries) overwritten with k_a/v_a in the same pass.  Returns out."""
+    entries) overwritten with k_a/v_a in the same pass.  active_idx None is the full
+    refresh (A == N, no cached rows): the caches become k_a/v_a.  Returns out."""
     B, H, A, D = q_a.shape
     N = k_cache.shape[2]
     dt = q_a.dtype
@@ -214,12 +215,15 @@ def mar_cache_attn_fwd_update(q_a, k_a, v_a, k_cache, v_cache, cached_idx, activ
         ldc = cached_idx.shape[1]
         Nc = ldc if Nc is None else int(Nc)
         cptr = _dev(cached_idx, "cached_idx", torch.int32)
-    if active_idx.dim() != 2 or active_idx.shape[0] != B or active_idx.stride(1) != 1:
-        raise ValueError("active_idx must be [B, ld] with unit column stride")
-    ld_act = active_idx.stride(0)
-    aptr = ctypes.c_void_p(active_idx.data_ptr())
-    if active_idx.dtype != torch.int32 or not active_idx.is_cuda:
-        raise ValueError("active_idx must be an int32 device tensor")
+    if active_idx is None:
+        ld_act, aptr = 0, None
+    else:
+        if active_idx.dim() != 2 or active_idx.shape[0] != B or active_idx.stride(1) != 1:
+            raise ValueError("active_idx must be [B, ld] with unit column stride")
+        ld_act = active_idx.stride(0)
+        aptr = ctypes.c_void_p(active_idx.data_ptr())
+        if active_idx.dtype != torch.int32 or not active_idx.is_cuda:
+            raise ValueError("active_idx must be an int32 device tensor")
     if out is None:
         out = torch.empty_like(q_a)
     _dev(out, "out", dt, (B, H, A, D))

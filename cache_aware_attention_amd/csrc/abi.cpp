@@ -88,11 +88,12 @@ extern "C" int mar_cache_attn_fwd_update(const void* q_a, const void* k_a, const
                                          int32_t* err_count, void* out, float* lse, int B, int H,
                                          int N, int A, int Nc, int D, float scale, int dtype,
                                          void* stream) {
-    if (!active_idx) return MAR_E_NULL;
     const int st = check_cache_attn(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, B, H,
                                     N, A, Nc, D, scale, dtype);
     if (st != MAR_OK) return st;
-    if (ld_act < A) return MAR_E_SHAPE;
+    // No list: a full refresh, which needs every token active.
+    if (!active_idx && !(A == N && Nc == 0)) return MAR_E_NULL;
+    if (active_idx && ld_act < A) return MAR_E_SHAPE;
     return marca::launch_cache_attn_update(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc,
                                            active_idx, ld_act, err_count, out, lse, B, H, N, A,
                                            Nc, scale, dtype, stream);

@@ -307,7 +307,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     const uint16_t* vc_u = v_cache + static_cast<size_t>(u) * N * kD;
     const int T = An + Ncn;
     const int nchunks = (T + kChunk - 1) / kChunk;
-    static_assert(!DENSE || (!UPDATE && !RAGGED), "dense rows: plain attention only");
+    static_assert(!DENSE || !RAGGED, "dense rows: uniform counts only");
     const __amdgpu_buffer_rsrc_t rka = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(ka_u), 0, An * kD * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rva = __builtin_amdgcn_make_buffer_rsrc(
@@ -379,7 +379,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 
     // Stage the cached list (entries outside [0, N) become -1).
     auto stage_list = [&]() __attribute__((always_inline)) {
-        if constexpr (DENSE) return;
+        if constexpr (DENSE && !UPDATE) return;
 #pragma unroll
         for (int k = 0; k < kIdxRegs; ++k) {
             const int c = lane + kWave * k;
@@ -390,13 +390,15 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
             cidx_s[c] = (n >= 0 && n < N) ? n : -1;
         }
         if constexpr (UPDATE) {
-            // Only the first query group of a unit writes its rows.  An entry
-            // outside [0, N) is skipped and, once per sequence, counted.
-            const int32_t* ag = active_idx + static_cast<size_t>(b) * ld_act;
-            for (int r = lane; r < An; r += kWave) {
-                const int n = ag[r];
+            // One query group writes each row (see the stores below).  An entry
+            // outside [0, N) is skipped and, once per sequence, counted.  With
+            // no list (A == N, a full refresh) row r goes to cache row r; the
+            // dense instantiation then needs no staged list at all.
+            const int32_t* ag = active_idx ? active_idx + static_cast<size_t>(b) * ld_act : nullptr;
+            for (int r = lane; r < An && (!DENSE || ag != nullptr); r += kWave) {
+                const int n = ag ? ag[r] : r;
                 const bool ok = n >= 0 && n < N;
-                aidx_s[r] = (ok && qg == 0) ? n : -1;
+                aidx_s[r] = (ok && (DENSE || qg == 0)) ? n : -1;
                 if (!ok && err_count != nullptr && qg == 0 && u % H == 0) atomicAdd(err_count, 1);
             }
         }
@@ -449,7 +451,11 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         for (int k = 0; k < 4; ++k)
             *reinterpret_cast<uint4*>(tile + vst + 1024 * k) = ch.v[k];
         if constexpr (UPDATE) {
-            if (c * kChunk < An) {  // wave-uniform: the chunk holds active rows
+            // wave-uniform: the chunk holds active rows, written by the
+            // unit's first query group (dense: every chunk holds active rows,
+            // and the query groups take turns, chunk c written by group
+            // c mod n_groups)
+            if (DENSE ? c % n_groups == qg : c * kChunk < An) {
                 // Buffer stores: an offset past the unit's N rows (inactive
                 // lane, skipped entry) is dropped by the range check.
                 constexpr uint32_t kSkip = 0x80000000u;
@@ -461,7 +467,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int r = c * kChunk + 16 * t + m16;
-                    const int n = (r < An) ? aidx_s[r] : -1;
+                    const int n = (r >= An) ? -1 : (DENSE && active_idx == nullptr) ? r : aidx_s[r];
                     const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.k[t][0]),
                                                            rk, off + 16 * g, 0, kNT);
@@ -471,7 +477,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int r = c * kChunk + 8 * k + (lane >> 3);
-                    const int n = (r < An) ? aidx_s[r] : -1;
+                    const int n = (r >= An) ? -1 : (DENSE && active_idx == nullptr) ? r : aidx_s[r];
                     const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.v[k]),
                                                            rv, off + 16 * (lane & 7), 0, kNT);
@@ -612,16 +618,16 @@ int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
     const int units = B * H;
     const int grid = (n_groups == 1) ? units : ((units + 7) / 8) * 8 * n_groups;
     constexpr size_t kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
+    const bool dense = a_len == nullptr && Nc == 0;  // no cached rows
+    const bool list = UPDATE && (active_idx != nullptr || !dense);
     const size_t lds = kTileBytes + static_cast<size_t>(Nc > 0 ? Nc : 1) * 4 +
-                       (UPDATE ? static_cast<size_t>(A) * 4 : 0);
-    if constexpr (!UPDATE) {
-        if (a_len == nullptr && Nc == 0) {
-            hipLaunchKernelGGL((attn_mfma_kernel<NQT, false, false, true>), dim3(grid), dim3(64),
-                               lds, stream, q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out,
-                               lse, units, H, N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
-                               err_count, a_len, c_len);
-            return status_from_launch();
-        }
+                       (list ? static_cast<size_t>(A) * 4 : 0);
+    if (dense) {
+        hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, false, true>), dim3(grid), dim3(64), lds,
+                           stream, q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
+                           units, H, N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
+                           err_count, a_len, c_len);
+        return status_from_launch();
     }
     if (a_len != nullptr)
         hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, true, false>), dim3(grid), dim3(64), lds,

@@ -129,14 +129,20 @@ int mar_cache_attn_fwd_ragged(const void* q_a, const void* k_a, const void* v_a,
  * -- the partial update of mar_kv_scatter_refresh with idx = active_idx and
  * M = A -- from the registers that already hold those rows, so the rows are
  * read from memory once.
- *   active_idx  [B,ld_act] int32: token positions of the A active rows.
+ *   active_idx  [B,ld_act] int32: token positions of the A active rows;
+ *               NULL means the full refresh of a refresh step ([MARche] Key
+ *               Design 3): every token is active (A == N, Nc == 0) and row i
+ *               goes to cache row i -- full attention over all N tokens
+ *               together with the cache rewrite of mar_kv_scatter_refresh
+ *               with idx = NULL.
  *   err_count   device int32, may be NULL: +1 per (sequence, entry) outside
  *               [0,N); such entries are skipped.
  * Precondition: the active positions of a sequence are distinct and none of
  * them is among its first Nc cached entries (the cached set is the
  * complement of the active set), so no cache row is both read and written;
  * otherwise the value read for such a row is unspecified.  Requirements and
- * errors as for mar_cache_attn_fwd, plus active_idx != NULL, ld_act >= A.
+ * errors as for mar_cache_attn_fwd, plus ld_act >= A when active_idx is
+ * given; active_idx == NULL with A != N or Nc != 0 returns MAR_E_NULL.
  */
 int mar_cache_attn_fwd_update(const void* q_a, const void* k_a, const void* v_a,
                               void* k_cache, void* v_cache,

@@ -80,7 +80,8 @@ def attn_upd(lib, q=P, ka=P, va=P, kc=P, vc=P, cidx=P, ldc=272, aidx=P, ld_act=4
 
 
 def test_cache_attn_update_rejections(lib):
-    assert attn_upd(lib, aidx=None) == E_NULL       # the active list is required
+    assert attn_upd(lib, aidx=None) == E_NULL       # the active list is required ...
+    assert attn_upd(lib, aidx=None, cidx=None, ldc=0, A=300, Nc=0) == E_NULL  # ... unless A == N
     assert attn_upd(lib, ld_act=47) == E_SHAPE      # ld_act < A
     assert attn_upd(lib, q=None) == E_NULL          # the attention's own checks apply
     assert attn_upd(lib, cidx=None) == E_NULL

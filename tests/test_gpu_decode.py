@@ -10,8 +10,8 @@ exactly as in decoding.  Per step:
 
 * the host plan (mar_plan_step) against the oracle's schedule;
 * refresh steps (t % 3 == 0): full attention of all N tokens and the full
-  cache rewrite, after which the cache equals the fresh K/V byte for byte;
-  the CFG residual is stored;
+  cache rewrite in one call, after which the cache equals the fresh K/V byte
+  for byte; the CFG residual is stored;
 * other steps: the top-K refresh selection from layer-2 scores (bit-exact on
   the GPU's scores; the partition covers every token once), the fused
   cache-aware attention + cache update (outputs against the oracle on the
@@ -86,16 +86,15 @@ def test_64_step_schedule(marca):
         uncond = cond - 0.1
         if plan.refresh:
             n_refresh_steps += 1
-            # every layer full attention; spot-check layer 3 on two units
-            out = marca.mar_cache_attn_fwd(q3, k3, v3, k3, v3, None, Nc=0)
+            # every layer full attention, and every cache row rewritten: layer 3
+            # does both in one call (no active list); spot-check two units
+            out = marca.mar_cache_attn_fwd_update(q3, k3, v3, kc, vc, None, None, Nc=0)
             torch.cuda.synchronize()
             for b, h in ((0, 0), (B - 1, H - 1)):
                 sl = lambda x: f64(x[b:b + 1, h:h + 1])
                 o, _ = oracle.cache_attention(sl(q3), sl(k3), sl(v3), sl(k3), sl(v3),
                                               np.zeros((1, 1), np.int32), scale, Nc=0)
                 assert np.abs(f64(out[b, h]) - o[0, 0]).max() <= 2e-2, f"step {t}"
-            marca.mar_kv_scatter_refresh(kc, vc, k3, v3, None)
-            torch.cuda.synchronize()
             assert torch.equal(kc, k3) and torch.equal(vc, v3), f"step {t}: full refresh"
             residual, _ = marca.mar_cfg_residual(cond, uncond)
             torch.cuda.synchronize()

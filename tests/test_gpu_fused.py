@@ -103,3 +103,36 @@ def test_fused_update_full_size_mar_l(marca):
     units = [(0, 0), (cfg.B - 1, cfg.H - 1)] + [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H)))
                                                 for _ in range(4)]
     assert check_case(marca, x, cfg.Nc, active, "bf16", units) == 0
+
+
+@pytest.mark.parametrize("dtype,B,H,N", [("bf16", 2, 3, 320), ("bf16", 2, 3, 200),
+                                         ("bf16", 3, 2, 77), ("bf16", 2, 2, 8),
+                                         ("f32", 2, 2, 40), ("bf16", 128, 16, 320)])
+def test_fused_full_refresh(marca, dtype, B, H, N):
+    """No active list: a refresh step's full attention over all N tokens and the
+    rewrite of every cache row, in one call.  The output equals the plain full
+    attention bit for bit, the caches equal the fresh K/V byte for byte, and
+    sampled units match the oracle."""
+    import oracle
+    from mar_workloads import device_normal
+    D = 64
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v, kc, vc = (device_normal((B, H, N, D), 300 + N + i, DEV, dt) for i in range(5))
+    lse_ref = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    out_ref = marca.mar_cache_attn_fwd(q, k, v, kc, vc, None, Nc=0, lse=lse_ref)
+    kc2, vc2 = kc.clone(), vc.clone()
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    out = marca.mar_cache_attn_fwd_update(q, k, v, kc2, vc2, None, None, Nc=0, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref) and torch.equal(lse, lse_ref)
+    assert np.array_equal(raw(kc2), raw(k)) and np.array_equal(raw(vc2), raw(v))
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        sl = lambda t: t[b:b + 1, h:h + 1].double().cpu().numpy()
+        o, l = oracle.cache_attention(sl(q), sl(k), sl(v), sl(kc), sl(vc),
+                                      np.zeros((1, 1), np.int32), D ** -0.5, Nc=0)
+        got = out[b, h].double().cpu().numpy()
+        if dtype == "bf16":
+            assert np.abs(got - o[0, 0]).max() <= 2e-2
+            assert np.abs(lse[b, h].double().cpu().numpy() - l[0, 0]).max() <= 2.5e-3
+        else:
+            assert np.abs(got - o[0, 0]).max() / np.abs(o[0, 0]).max() <= 1e-5
