@@ -19,9 +19,11 @@
 //    ds_read_b64_tr_b16 as the PV operand.  The next chunk's loads are issued
 //    before the current chunk is computed.  The unit's cached index list is
 //    staged in LDS once.  Separate instantiations serve per-sequence counts,
-//    the fused cache update, and the case with no cached rows (the
-//    full-attention layers), whose keys are contiguous rows read at fixed
-//    per-lane offsets.
+//    the fused cache update, and the case with no cached rows, whose keys are
+//    contiguous rows read at fixed per-lane offsets.
+//  * attn_dense_wg_kernel (bf16, no cached rows, A > 64: the full-attention
+//    layers): a 4-wave workgroup per 320 queries of a unit shares each K/V
+//    chunk through a double-buffered LDS tile; same per-tile arithmetic.
 //  * attn_rowwise_kernel (fp32 any A, bf16 A < 16): one wave per query, one
 //    lane per head-dim element; plain FMA.  Exact-precision path for fp32.
 //
@@ -608,6 +610,269 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     }
 }
 
+// ---------------------------------------------------------------------------
+// Dense workgroup kernel: all tokens active and no cached rows (the
+// full-attention layers, and with UPDATE a refresh step's layer).  One
+// workgroup of kWgWaves waves per (unit, block of kWgWaves * 16 * NQT
+// queries); NQT = 5 makes one workgroup cover a 320-token unit.  Each 32-row
+// K/V chunk is loaded once per workgroup -- every lane one 16-byte piece of K
+// and one of V -- into a double-buffered LDS tile, and every wave reads its
+// MFMA operands from there.  A unit's K/V then crosses the L2-to-CU path once
+// per workgroup instead of once per 64-query wave, which is what bounds the
+// one-wave kernel at these sizes.  With UPDATE the loading lanes also write
+// their pieces into the caches (row r to cache row r).  The arithmetic per
+// 16-query tile is that of attn_mfma_kernel, chunk for chunk, so both give
+// the same bits.
+// ---------------------------------------------------------------------------
+constexpr int kWgWaves = 4;
+constexpr int kWgNqt = 5;
+constexpr int kWgTile = kChunk * 128;  // bytes of one K or V chunk tile
+
+template <int NQT, bool UPDATE>
+__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
+                          const uint16_t* __restrict__ v_a, uint16_t* k_cache, uint16_t* v_cache,
+                          uint16_t* __restrict__ out, float* __restrict__ lse, int units, int A,
+                          int n_blocks, float scale_log2) {
+    constexpr int kQ = 16 * NQT;  // queries per wave
+    __shared__ __align__(16) unsigned char lds[4 * kWgTile];  // 2 buffers x (K tile, V tile)
+    static_assert(4 * kWgTile >= kWgWaves * 2048, "the output staging reuses the K/V tiles");
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int g = lane >> 4;
+    const int m16 = lane & 15;
+
+    int u, qb;
+    if (n_blocks == 1) {
+        u = blockIdx.x;
+        qb = 0;
+    } else {  // the blocks of one unit on one XCD (workgroups go round-robin over the 8)
+        const int xcd = blockIdx.x & 7;
+        const int slot = blockIdx.x >> 3;
+        u = (slot / n_blocks) * 8 + xcd;
+        qb = slot % n_blocks;
+        if (u >= units) return;  // uniform over the workgroup, before any barrier
+    }
+    const int q0 = (qb * kWgWaves + w) * kQ;
+    const int nq = min(A - q0, kQ);  // <= 0: the wave loads and waits, computes nothing
+    const size_t ub = static_cast<size_t>(u) * A * kD;
+    const int nchunks = (A + kChunk - 1) / kChunk;
+    const __amdgpu_buffer_rsrc_t rka = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(k_a + ub), 0, A * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rva = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(v_a + ub), 0, A * kD * 2, 0x00020000);
+
+    // Loading lane: piece tid % 8 of row tid / 8 of the chunk, for K and V.
+    // A row past A reads as zero (range-checked buffer load).
+    const int lrow = tid >> 3;
+    const int gofs = lrow * (kD * 2) + 16 * (tid & 7);
+    const int lofs = swz(lrow, tid & 7);
+    auto load = [&](int c, uint4& kk, uint4& vv) __attribute__((always_inline)) {
+        const int rb = c * kChunk * (kD * 2);
+        kk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rka, rb + gofs, 0, 0));
+        vv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rva, rb + gofs, 0, 0));
+    };
+    auto put = [&](int buf, int c, const uint4& kk, const uint4& vv) __attribute__((always_inline)) {
+        *reinterpret_cast<uint4*>(lds + buf * 2 * kWgTile + lofs) = kk;
+        *reinterpret_cast<uint4*>(lds + buf * 2 * kWgTile + kWgTile + lofs) = vv;
+        if constexpr (UPDATE) {
+            // A row past A, or the repeated last chunk (c >= nchunks), gets an
+            // offset past the buffer: the range check drops the store.
+            constexpr uint32_t kSkip = 0x80000000u;
+            constexpr int kNT = 2;  // nontemporal (streaming) store
+            const int r = c * kChunk + lrow;
+            const uint32_t off = (c < nchunks && r < A)
+                                     ? static_cast<uint32_t>(c * kChunk * (kD * 2) + gofs)
+                                     : kSkip;
+            const __amdgpu_buffer_rsrc_t rk =
+                __builtin_amdgcn_make_buffer_rsrc(k_cache + ub, 0, A * kD * 2, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc(v_cache + ub, 0, A * kD * 2, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, kk), rk, off, 0, kNT);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vv), rv, off, 0, kNT);
+        }
+    };
+
+    // Q operands (B of S^T = K Q^T): lane holds query m16 of tile qt, head
+    // dims [8g, 8g+8) and [32+8g, 32+8g+8).  Rows past the end load the last
+    // query; they are never stored.
+    bf16x8_t qf[NQT][2];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        const int qi = max(min(q0 + qt * 16 + m16, A - 1), 0);
+        const uint4* p = reinterpret_cast<const uint4*>(q_a + ub + static_cast<size_t>(qi) * kD);
+        qf[qt][0] = as_bf16x8(p[g]);
+        qf[qt][1] = as_bf16x8(p[4 + g]);
+    }
+    // LDS byte offsets: the V^T transposing reads as in attn_mfma_kernel, and
+    // the K operand pieces g and 4+g of key row 16t + m16.
+    int vofs[2][4], kofs[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            vofs[h][dt] = swz(16 * h + 4 * g + (m16 >> 2), 2 * dt + ((m16 & 3) >> 1)) +
+                          ((m16 & 1) << 3);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        kofs[t][0] = swz(16 * t + m16, g);
+        kofs[t][1] = swz(16 * t + m16, 4 + g);
+    }
+
+    const float thr_raw = kRescaleLog2 / scale_log2;
+    float mref[NQT], mc[NQT], mthr[NQT];
+    f32x4_t oacc[NQT][4], lacc[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        mref[qt] = -INFINITY;
+        mthr[qt] = -INFINITY;
+        mc[qt] = 0.f;
+        lacc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+
+    auto compute = [&](int c, int buf) __attribute__((always_inline)) {
+        const unsigned char* kt = lds + buf * 2 * kWgTile;
+        const unsigned char* vt = kt + kWgTile;
+        uint4 kop[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            kop[t][0] = *reinterpret_cast<const uint4*>(kt + kofs[t][0]);
+            kop[t][1] = *reinterpret_cast<const uint4*>(kt + kofs[t][1]);
+        }
+        bf16x8_t va[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const uint2 lo = lds_tr_b64(vt + vofs[0][dt]);
+            const uint2 hi = lds_tr_b64(vt + vofs[1][dt]);
+            va[dt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
+        const int r0 = c * kChunk;
+        const bool full = r0 + kChunk <= A;  // wave-uniform
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            if (qt * 16 >= nq) continue;  // wave-uniform
+            f32x4_t s[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[t][0]), qf[qt][0], acc,
+                                                              0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[t][1]), qf[qt][1], acc,
+                                                              0, 0, 0);
+                s[t] = acc;
+            }
+            if (!full) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (r0 + 16 * t + 4 * g + i >= A) s[t][i] = -INFINITY;
+            }
+            const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+            if (__any(mx > mthr[qt])) {  // a query's maximum moved far up: rescale
+                const float mnew = fmaxf(mref[qt], max_over_groups(mx));
+                const float alpha = (mref[qt] == -INFINITY)
+                                        ? 0.f
+                                        : __builtin_amdgcn_exp2f((mref[qt] - mnew) * scale_log2);
+                lacc[qt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] *= alpha;
+                mref[qt] = mnew;
+                mc[qt] = mnew * scale_log2;
+                mthr[qt] = mnew + thr_raw;
+            }
+            float p[8];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(s[t][i], scale_log2, -mc[qt]));
+            U4 pk;
+            pk.u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                              pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+            lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk.v, lacc[qt], 0, 0, 0);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk.v,
+                                                                       oacc[qt][dt], 0, 0, 0);
+        }
+    };
+
+    // Chunk c sits in LDS buffer c % 2.  Each step requests chunk c + 1 into
+    // the staging registers, computes chunk c, stores chunk c + 1 into the
+    // other buffer (whose chunk c - 1 every wave finished before the previous
+    // barrier) and waits at the barrier.  Every step issues the same loads
+    // (past the end the last chunk is requested again and not used), so the
+    // compiler's memory-counter waits stay exact.
+    uint4 sk, sv;
+    load(0, sk, sv);
+    put(0, 0, sk, sv);
+    __syncthreads();
+    auto step = [&](int c, auto buf_tag) __attribute__((always_inline)) {
+        constexpr int BI = decltype(buf_tag)::value;
+        load(min(c + 1, nchunks - 1), sk, sv);
+        if (nq > 0) compute(c, BI);
+        put(BI ^ 1, c + 1, sk, sv);
+        __syncthreads();
+    };
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        step(c, std::integral_constant<int, 0>{});
+        step(c + 1, std::integral_constant<int, 1>{});
+    }
+    if (c < nchunks) step(c, std::integral_constant<int, 0>{});
+
+    // Finalise through this wave's 2 KB of the (now free) LDS tiles, one
+    // 16-query tile at a time, so that every (nontemporal) store writes
+    // whole 128-byte rows.
+    if (nq <= 0) return;
+    unsigned char* ot = lds + w * 2048;
+    u32x4_t* orow = reinterpret_cast<u32x4_t*>(out + ub + static_cast<size_t>(q0) * kD);
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        if (qt * 16 >= nq) continue;
+        const float l = lacc[qt][0];
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const uint2 v2 = make_uint2(pack_bf16x2(oacc[qt][dt][0] * inv, oacc[qt][dt][1] * inv),
+                                        pack_bf16x2(oacc[qt][dt][2] * inv, oacc[qt][dt][3] * inv));
+            *reinterpret_cast<uint2*>(ot + swz(m16, 2 * dt + (g >> 1)) + ((g & 1) << 3)) = v2;
+        }
+        const int row = 16 * qt + m16;
+        if (lse != nullptr && g == 0 && row < nq)
+            lse[static_cast<size_t>(u) * A + q0 + row] = (mc[qt] + log2f(l)) * kLn2;
+        __builtin_amdgcn_wave_barrier();  // the tile's writes before its reads (one wave)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int r = 8 * k + (lane >> 3);
+            const u32x4_t v4 = *reinterpret_cast<const u32x4_t*>(ot + swz(r, lane & 7));
+            if (16 * qt + r < nq)
+                __builtin_nontemporal_store(v4, orow + (16 * qt + r) * 8 + (lane & 7));
+        }
+        __builtin_amdgcn_wave_barrier();  // the reads before the next tile's writes
+    }
+}
+
+template <bool UPDATE>
+int launch_dense_wg(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
+                    uint16_t* k_cache, uint16_t* v_cache, uint16_t* out, float* lse, int B, int H,
+                    int A, float scale_log2, hipStream_t stream) {
+    const int units = B * H;
+    constexpr int kPerBlock = kWgWaves * 16 * kWgNqt;
+    const int nb = (A + kPerBlock - 1) / kPerBlock;
+    const int grid = (nb == 1) ? units : ((units + 7) / 8) * 8 * nb;
+    hipLaunchKernelGGL((attn_dense_wg_kernel<kWgNqt, UPDATE>), dim3(grid), dim3(64 * kWgWaves), 0,
+                       stream, q_a, k_a, v_a, k_cache, v_cache, out, lse, units, A, nb,
+                       scale_log2);
+    return status_from_launch();
+}
+
 template <int NQT, bool UPDATE>
 int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
                 const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* cached_idx,
@@ -648,6 +913,14 @@ int dispatch_mfma(const uint16_t* q, const uint16_t* ka, const uint16_t* va, con
                   int B, int H, int N, int A, int Nc, float scale_log2, const int32_t* active_idx,
                   int ld_act, int32_t* err_count, const int32_t* a_len, const int32_t* c_len,
                   hipStream_t stream) {
+    // All tokens active and no cached rows, more queries than one wave holds:
+    // the workgroup kernel (with UPDATE only for the full refresh, row r to
+    // cache row r).
+    if (a_len == nullptr && Nc == 0 && A > kQueriesPerGroup &&
+        (!UPDATE || active_idx == nullptr))
+        return launch_dense_wg<UPDATE>(q, ka, va, const_cast<uint16_t*>(kc),
+                                       const_cast<uint16_t*>(vc), o, lse, B, H, A, scale_log2,
+                                       stream);
     const int n_groups = (A + kQueriesPerGroup - 1) / kQueriesPerGroup;
     const int nqt = (n_groups > 1) ? 4 : (A + 15) / 16;
     switch (nqt) {

@@ -3,6 +3,8 @@
 * attention: the largest token count the MFMA path takes (N = 8192, a 32 KB
   staged cached list), one past it (the row-wise path takes over), a cached
   list whose entries are all invalid, and a single (sequence, head) unit;
+* full attention (no cached rows) over 4096 and 1088 tokens, several
+  workgroups per unit with a partly idle last one, also with the full refresh;
 * top-K: the largest N (4096, two-pass scores and LDS-read ranking), repeated
   G/P entries, every token taken (empty cached list);
 * gate: a width above the multi-token kernel's range (one token per wave);
@@ -138,3 +140,29 @@ def test_scatter_every_row(marca):
     torch.cuda.synchronize()
     assert skipped == 0
     assert np.array_equal(raw(k2), rk) and np.array_equal(raw(v2), rv)
+
+
+@pytest.mark.parametrize("B,H,N,update", [(1, 2, 4096, False), (2, 2, 1088, False),
+                                          (2, 2, 1088, True), (3, 1, 130, True)])
+def test_full_attention_long_and_partial_blocks(marca, B, H, N, update):
+    """All tokens active, no cached rows, more than one 320-query workgroup per
+    (sequence, head) and a last workgroup with idle waves; with the full
+    refresh the caches must become the fresh K/V exactly."""
+    import oracle
+    D = 64
+    q, k, v, kc, vc = (device_normal((B, H, N, D), 700 + N + i, DEV, torch.bfloat16)
+                       for i in range(5))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    if update:
+        out = marca.mar_cache_attn_fwd_update(q, k, v, kc, vc, None, None, Nc=0, lse=lse)
+    else:
+        out = marca.mar_cache_attn_fwd(q, k, v, kc, vc, None, Nc=0, lse=lse)
+    torch.cuda.synchronize()
+    if update:
+        assert torch.equal(kc, k) and torch.equal(vc, v)
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        sl = lambda t: f64(t[b:b + 1, h:h + 1])
+        o, l = oracle.cache_attention(sl(q), sl(k), sl(v), sl(k), sl(v),
+                                      np.zeros((1, 1), np.int32), D ** -0.5, Nc=0)
+        assert np.abs(f64(out[b, h]) - o[0, 0]).max() <= 2e-2
+        assert np.abs(f64(lse[b, h]) - l[0, 0]).max() <= 2.5e-3
