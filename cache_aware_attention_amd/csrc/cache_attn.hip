@@ -734,7 +734,8 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
     }
     const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
-    auto compute = [&](int c, int buf) __attribute__((always_inline)) {
+    auto compute = [&](int c, int buf, auto full_tag) __attribute__((always_inline)) {
+        constexpr bool kFull = decltype(full_tag)::value;  // no row of the chunk past A
         const unsigned char* kt = lds + buf * 2 * kWgTile;
         const unsigned char* vt = kt + kWgTile;
         uint4 kop[2][2];
@@ -751,7 +752,6 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
             va[dt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
         const int r0 = c * kChunk;
-        const bool full = r0 + kChunk <= A;  // wave-uniform
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
             if (qt * 16 >= nq) continue;  // wave-uniform
@@ -765,7 +765,7 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
                                                               0, 0, 0);
                 s[t] = acc;
             }
-            if (!full) {
+            if constexpr (!kFull) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -774,7 +774,9 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
             }
             const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-            if (__any(mx > mthr[qt])) {  // a query's maximum moved far up: rescale
+            // A query's maximum moved far up: rescale (rare; kept off the
+            // straight-line path so it is not turned into selects).
+            if (__builtin_expect(__any(mx > mthr[qt]), 0)) {
                 const float mnew = fmaxf(mref[qt], max_over_groups(mx));
                 const float alpha = (mref[qt] == -INFINITY)
                                         ? 0.f
@@ -813,19 +815,31 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
     load(0, sk, sv);
     put(0, 0, sk, sv);
     __syncthreads();
-    auto step = [&](int c, auto buf_tag) __attribute__((always_inline)) {
+    auto step = [&](int c, auto buf_tag, auto full_tag) __attribute__((always_inline)) {
         constexpr int BI = decltype(buf_tag)::value;
         load(min(c + 1, nchunks - 1), sk, sv);
-        if (nq > 0) compute(c, BI);
+        if (nq > 0) compute(c, BI, full_tag);
         put(BI ^ 1, c + 1, sk, sv);
         __syncthreads();
     };
+    // The chunks without rows past A, in pairs (constant buffer indices),
+    // then the partial last chunk if A is not a multiple of 32: only that
+    // one carries the masking.
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    const int nfull = A / kChunk;
     int c = 0;
-    for (; c + 1 < nchunks; c += 2) {
-        step(c, std::integral_constant<int, 0>{});
-        step(c + 1, std::integral_constant<int, 1>{});
+    for (; c + 1 < nfull; c += 2) {
+        step(c, B0{}, std::true_type{});
+        step(c + 1, B1{}, std::true_type{});
     }
-    if (c < nchunks) step(c, std::integral_constant<int, 0>{});
+    if (c < nfull) step(c++, B0{}, std::true_type{});
+    if (c < nchunks) {
+        if (c & 1)
+            step(c, B1{}, std::false_type{});
+        else
+            step(c, B0{}, std::false_type{});
+    }
 
     // Finalise through this wave's 2 KB of the (now free) LDS tiles, one
     // 16-query tile at a time, so that every (nontemporal) store writes
