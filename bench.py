@@ -7,7 +7,9 @@ CFG = 128 sequences, 16 heads x 64, N = 320 tokens, active 48 = 16 generating
   * the host step plan (refresh decision, budget-filled K);
   * layer 2: refresh scores + top-K + active/cached partition (mar_refresh_topk);
   * layers 3..32 (30 layers): cache-aware attention (mar_cache_attn_fwd) and the
-    K/V scatter of the active rows into that layer's cache (mar_kv_scatter_refresh);
+    K/V scatter of the active rows into that layer's cache (mar_kv_scatter_refresh),
+    the scatters on a second stream so they overlap the following layers'
+    attention (they touch rows no later layer reads);
   * the CFG condition cache reuse on the 16-channel token outputs (mar_cfg_residual);
   * one cosine-gate evaluation on the 1024-wide hidden features (mar_cos_gate).
 
@@ -222,6 +224,13 @@ def main():
 
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    # The K/V scatters run on a second stream (default priority).  Layer l's
+    # scatter writes the active rows of layer l's cache, which no later layer
+    # reads, so it only has to wait until layer l's fresh K/V exist (layer
+    # l - 1 done); the step ends by joining the two streams.
+    side = torch.cuda.Stream()
+    layer_done = [torch.cuda.Event() for _ in range(cfg.layers)]
+    side_done = torch.cuda.Event()
 
     def topk(plan):
         marca.mar_refresh_topk(x["q_gen"], x["k_full"], x["gp"], plan.n_prev + plan.n_gen,
@@ -234,10 +243,22 @@ def main():
         marca.mar_cache_attn_fwd(L["q_a"], L["k_a"], L["v_a"], L["k_cache"], L["v_cache"],
                                  x["cached_idx"], Nc=plan.n_cached, out=L["out"])
 
-    def scatter(l):
+    def scatter(l, on=None):
         L = x["layers"][l]
         marca.mar_kv_scatter_refresh(L["k_cache"], L["v_cache"], L["k_a"], L["v_a"],
-                                     x["active_idx"])
+                                     x["active_idx"], stream=on)
+
+    def cached_layers(plan):
+        """Layers 3-32 of a cached step: attention on the main stream, each
+        layer's scatter on the side stream once the previous layer is done."""
+        layer_done[0].record(stream)
+        for l in range(n_ca):
+            side.wait_event(layer_done[l])
+            scatter(l, on=side)
+            attn(l, plan)
+            layer_done[l + 1].record(stream)
+        side_done.record(side)
+        stream.wait_event(side_done)
 
     def fused(l, plan):
         L = x["layers"][l]
@@ -268,12 +289,11 @@ def main():
 
     def one_step():
         """One decode step in model order: top-K at layer 2, then per cache-aware
-        layer its attention and the scatter of its fresh rows, then CFG + gate."""
+        layer its attention and the scatter of its fresh rows (overlapped on the
+        side stream), then CFG + gate."""
         plan = plan_step()
         topk(plan)
-        for l in range(n_ca):
-            attn(l, plan)
-            scatter(l)
+        cached_layers(plan)
         cfg_reuse()
         gate()
 
@@ -319,9 +339,7 @@ def main():
             full_attn(0)
             full_attn(1)
             topk(plan)
-            for l in range(n_ca):
-                attn(l, plan)
-                scatter(l)
+            cached_layers(plan)
             cfg_reuse()
             gate()
 
