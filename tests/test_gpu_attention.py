@@ -207,6 +207,37 @@ def test_full_attention_mar_l_layer(marca):
         check(np64(out[b, h])[None], np64(lse[b, h])[None], o[0], l[0], "bf16")
 
 
+@pytest.mark.parametrize("name,update", [("mar_h", False), ("highres", False),
+                                         ("highres", True)])
+def test_full_attention_full_size(marca, name, update):
+    """Full-attention layers at the MAR-H shape (256 sequences, 20 heads,
+    N = 320) and the high-res shape (N = 1088: four workgroups per unit, the
+    last with idle waves); with the update, a refresh step's layer, whose
+    caches must come out equal to the fresh K/V."""
+    from mar_workloads import device_normal
+    import oracle
+    cfg = CONFIGS[name]
+    B, H, N = cfg.B, cfg.H, cfg.N
+    q, k, v = (device_normal((B, H, N, 64), 310 + i, DEV, torch.bfloat16) for i in range(3))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    if update:
+        kc, vc = torch.zeros_like(k), torch.zeros_like(v)
+        out = marca.mar_cache_attn_fwd_update(q, k, v, kc, vc, None, None, Nc=0, lse=lse)
+    else:
+        out = marca.mar_cache_attn_fwd(q, k, v, k, v, None, Nc=0, lse=lse)
+    torch.cuda.synchronize()
+    if update:
+        assert torch.equal(kc, k) and torch.equal(vc, v)
+        del kc, vc
+    rng = np.random.default_rng(cfg.seed + 1)
+    units = [(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))]
+    for b, h in units:
+        sl = lambda t: np64(t[b:b + 1, h:h + 1])
+        o, l = oracle.cache_attention(sl(q), sl(k), sl(v), sl(k), sl(v),
+                                      np.zeros((1, 1), np.int32), 0.125, Nc=0)
+        check(np64(out[b, h])[None], np64(lse[b, h])[None], o[0], l[0], "bf16")
+
+
 @pytest.mark.parametrize("name", ["mar_b", "mar_l", "mar_h", "highres"])
 def test_full_size_sampled_units(marca, name):
     """Full-size MAR shapes, the launch configuration the benchmark times;
