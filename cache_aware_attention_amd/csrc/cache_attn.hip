@@ -250,12 +250,17 @@ struct ChunkRegs {
 // one unit never touch the same row and different units never share a row.
 // RAGGED: per-sequence active / cached counts from a_len / c_len (a separate
 // instantiation, so the uniform-count kernel carries none of it).
+// SPLIT > 1: few units (small batches).  A workgroup of SPLIT waves per unit,
+// each wave streaming its own contiguous range of the unit's chunks; the
+// waves' partial (max, sum, weighted sum) states are then merged pairwise
+// through LDS with the same rule as the chunk-to-chunk merge, and the first
+// wave writes the output.
 // DENSE: no cached rows (Nc == 0, the full-attention layers): the unit's keys
 // are rows 0..A-1 of k_a/v_a, read with range-checked buffer loads at
 // per-lane offsets fixed for the whole sequence.  A row past A reads as zero
 // and is masked like a missing row.
-template <int NQT, bool UPDATE, bool RAGGED, bool DENSE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
+template <int NQT, bool UPDATE, bool RAGGED, bool DENSE, int SPLIT = 1>
+__global__ __launch_bounds__(64 * SPLIT) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
                       const uint16_t* __restrict__ v_a, const uint16_t* k_cache,
                       const uint16_t* v_cache, const int32_t* __restrict__ cached_idx, int ldc,
@@ -267,12 +272,20 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     constexpr int kPF = prefetch_depth(NQT);
     static_assert(kPF >= 1 && kPF <= 3, "prefetch depth");
     constexpr int kTileBytes = (16 * NQT * 128 > kChunk * 128) ? 16 * NQT * 128 : kChunk * 128;
+    static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4 || SPLIT == 8, "split");
+    // With SPLIT > 1 each wave has its own V tile; after the chunks the same
+    // bytes hold the partial states being merged (kState floats per lane).
+    constexpr int kState = NQT * 18;  // per tile: 16 weighted sums, max, sum
+    constexpr int kRegionBytes = (SPLIT / 2) * 64 * kState * 4 > SPLIT * kTileBytes
+                                     ? (SPLIT / 2) * 64 * kState * 4
+                                     : SPLIT * kTileBytes;
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* tile = smem;  // V chunk, later the output tile
-    int32_t* cidx_s = reinterpret_cast<int32_t*>(smem + kTileBytes);  // [max(Nc, 1)]
-    int32_t* aidx_s = cidx_s + (Nc > 0 ? Nc : 1);                     // [A] with UPDATE
+    const int wv = (SPLIT > 1) ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+    unsigned char* tile = smem + wv * kTileBytes;  // V chunk, later the output tile
+    int32_t* cidx_s = reinterpret_cast<int32_t*>(smem + kRegionBytes);  // [max(Nc, 1)]
+    int32_t* aidx_s = cidx_s + (Nc > 0 ? Nc : 1);                       // [A] with UPDATE
 
-    const int lane = threadIdx.x;
+    const int lane = (SPLIT > 1) ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
     const int g = lane >> 4;    // lane group: k-slot group of the MFMA operands
     const int m16 = lane & 15;  // row / column within a 16x16 tile
 
@@ -309,6 +322,13 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     const uint16_t* vc_u = v_cache + static_cast<size_t>(u) * N * kD;
     const int T = An + Ncn;
     const int nchunks = (T + kChunk - 1) / kChunk;
+    // This wave's chunks [cb, ce) (all of them unless SPLIT > 1).
+    int cb = 0, ce = nchunks;
+    if constexpr (SPLIT > 1) {
+        const int per = (nchunks + SPLIT - 1) / SPLIT;
+        cb = min(wv * per, nchunks);
+        ce = min(cb + per, nchunks);
+    }
     static_assert(!DENSE || !RAGGED, "dense rows: uniform counts only");
     const __amdgpu_buffer_rsrc_t rka = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(ka_u), 0, An * kD * 2, 0x00020000);
@@ -401,7 +421,8 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
                 const int n = ag ? ag[r] : r;
                 const bool ok = n >= 0 && n < N;
                 aidx_s[r] = (ok && (DENSE || qg == 0)) ? n : -1;
-                if (!ok && err_count != nullptr && qg == 0 && u % H == 0) atomicAdd(err_count, 1);
+                if (!ok && err_count != nullptr && qg == 0 && u % H == 0 && wv == 0)
+                    atomicAdd(err_count, 1);
             }
         }
         __syncthreads();  // one wave: orders the list writes before the reads below
@@ -412,15 +433,30 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     // When the sequence has fewer than kPF chunks the spare buffers load its
     // last chunk again (never used), so every path issues the same loads.
     ChunkRegs cr[kPF + 1];
-    if (An >= kChunk) {
-        issue(0, cr[0]);
-        stage_list();
-    } else {
-        stage_list();
-        issue(0, cr[0]);
-    }
+    if constexpr (SPLIT == 1) {
+        if (An >= kChunk) {
+            issue(0, cr[0]);
+            stage_list();
+        } else {
+            stage_list();
+            issue(0, cr[0]);
+        }
 #pragma unroll
-    for (int k = 1; k < kPF; ++k) issue(min(k, nchunks - 1), cr[k]);
+        for (int k = 1; k < kPF; ++k) issue(min(k, nchunks - 1), cr[k]);
+    } else {
+        // A wave with no chunks (cb == ce) requests the unit's last chunk
+        // and never computes it.
+        const int c0 = min(cb, nchunks - 1);
+        if ((c0 + 1) * kChunk <= An) {
+            issue(c0, cr[0]);
+            stage_list();
+        } else {
+            stage_list();
+            issue(c0, cr[0]);
+        }
+#pragma unroll
+        for (int k = 1; k < kPF; ++k) issue(max(min(cb + k, ce - 1), c0), cr[k]);
+    }
     // Per-lane LDS byte offsets of the V^T transposing reads: lane s of its
     // 16-lane group addresses key row 16h + 4g + s/4, head dims 16dt + 4(s%4).
     int vofs[2][4];
@@ -560,24 +596,76 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         constexpr int BI = decltype(buf_tag)::value;
         constexpr int BN = (BI + kPF) % (kPF + 1);
         __builtin_amdgcn_s_setprio(3);  // requests first: they keep HBM busy
-        issue(min(c + kPF, nchunks - 1), cr[BN]);
+        issue(min(c + kPF, ce - 1), cr[BN]);
         __builtin_amdgcn_s_setprio(0);
         compute(c, cr[BI]);
     };
     // Whole groups without guards (so the state at the loop back edge is the
     // same on every path), then the last nchunks mod (kPF + 1) chunks.
-    int c = 0;
-    for (; c + kPF < nchunks; c += kPF + 1) {
+    int c = cb;
+    for (; c + kPF < ce; c += kPF + 1) {
         step(c, std::integral_constant<int, 0>{});
         step(c + 1, std::integral_constant<int, 1>{});
         if constexpr (kPF >= 2) step(c + 2, std::integral_constant<int, 2>{});
         if constexpr (kPF >= 3) step(c + 3, std::integral_constant<int, 3>{});
     }
-    if (c < nchunks) step(c, std::integral_constant<int, 0>{});
+    if (c < ce) step(c, std::integral_constant<int, 0>{});
     if constexpr (kPF >= 2)
-        if (c + 1 < nchunks) step(c + 1, std::integral_constant<int, 1>{});
+        if (c + 1 < ce) step(c + 1, std::integral_constant<int, 1>{});
     if constexpr (kPF >= 3)
-        if (c + 2 < nchunks) step(c + 2, std::integral_constant<int, 2>{});
+        if (c + 2 < ce) step(c + 2, std::integral_constant<int, 2>{});
+
+    if constexpr (SPLIT > 1) {
+        // Pairwise merge: in round r the wave r past a multiple of 2r hands
+        // its state to that multiple through LDS.  A state whose maximum is
+        // still -inf (the wave saw no valid key) contributes nothing.
+        float* mbuf = reinterpret_cast<float*>(smem);
+        __syncthreads();  // every wave is done with its V tile
+#pragma unroll
+        for (int r = 1; r < SPLIT; r <<= 1) {
+            float* st = mbuf + (wv / (2 * r)) * (64 * kState);
+            if ((wv & (2 * r - 1)) == r) {
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt) {
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            st[(qt * 18 + 4 * dt + i) * 64 + lane] = oacc[qt][dt][i];
+                    st[(qt * 18 + 16) * 64 + lane] = mref[qt];
+                    st[(qt * 18 + 17) * 64 + lane] = lacc[qt][0];
+                }
+            }
+            __syncthreads();
+            if ((wv & (2 * r - 1)) == 0) {
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt) {
+                    const float mb = st[(qt * 18 + 16) * 64 + lane];
+                    const float lb = st[(qt * 18 + 17) * 64 + lane];
+                    const bool va = mref[qt] != -INFINITY;
+                    const bool vb = mb != -INFINITY;
+                    const float mcb = mb * scale_log2;
+                    const float mcm = fmaxf(va ? mc[qt] : -INFINITY, vb ? mcb : -INFINITY);
+                    const float fa = va ? __builtin_amdgcn_exp2f(mc[qt] - mcm) : 0.f;
+                    const float fb = vb ? __builtin_amdgcn_exp2f(mcb - mcm) : 0.f;
+                    const float l = lacc[qt][0] * fa + lb * fb;
+                    lacc[qt] = f32x4_t{l, l, l, l};
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            oacc[qt][dt][i] =
+                                oacc[qt][dt][i] * fa + st[(qt * 18 + 4 * dt + i) * 64 + lane] * fb;
+                    if (vb && (!va || mb > mref[qt])) {
+                        mref[qt] = mb;
+                        mc[qt] = mcb;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        if (wv != 0) return;  // after the last barrier
+    }
 
     // Finalise: lane holds O[query 16qt + m16][16dt + 4g + i] = oacc[qt][dt][i]
     // and the softmax denominator of that query in every lacc[qt][i].  The
@@ -598,7 +686,10 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         if (lse != nullptr && g == 0 && row < nq)
             lse[static_cast<size_t>(u) * A + qi] = (mc[qt] + log2f(l)) * kLn2;
     }
-    __syncthreads();
+    if constexpr (SPLIT > 1)
+        __builtin_amdgcn_wave_barrier();  // only the first wave is left
+    else
+        __syncthreads();  // one wave: orders the tile writes before the reads
     u32x4_t* orow = reinterpret_cast<u32x4_t*>(out + (static_cast<size_t>(u) * A + q0) * kD);
 #pragma unroll
     for (int k = 0; k < 2 * NQT; ++k) {
@@ -921,6 +1012,88 @@ int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
     return status_from_launch();
 }
 
+// Waves per workgroup for few units: double while the (unit, group) count
+// times the waves stays within a quarter of the chip's wave slots (256 CUs x
+// 8; with more work items the one-wave kernel already keeps HBM busy, and a
+// split of 768 MAR-B units measured slower) and every wave keeps at least one
+// chunk; 4 at most with 64 queries per group (the merge's LDS).
+constexpr int kWaveSlots = 2048 / 4;
+constexpr size_t split_region(int nqt, int split) {
+    const size_t tile = (16 * nqt * 128 > kChunk * 128) ? 16 * nqt * 128 : kChunk * 128;
+    const size_t merge = static_cast<size_t>(split / 2) * 64 * nqt * 18 * 4;
+    return merge > split * tile ? merge : split * tile;
+}
+inline size_t split_lds(int nqt, int split, bool update, int A, int Nc) {
+    return split_region(nqt, split) + static_cast<size_t>(Nc > 0 ? Nc : 1) * 4 +
+           (update ? static_cast<size_t>(A) * 4 : 0);
+}
+inline int split_for(int units, int n_groups, int nchunks, int nqt) {
+    const int cap = (nqt >= 4) ? 4 : 8;
+    int s = 1;
+    while (s < cap && static_cast<long>(units) * n_groups * 2 * s <= kWaveSlots &&
+           nchunks >= 2 * s)
+        s *= 2;
+    return s;
+}
+
+// SPLIT > 1: one workgroup of SPLIT waves per (unit, query group).
+template <int NQT, bool UPDATE, int SPLIT>
+int launch_split(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
+                 const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* cached_idx,
+                 int ldc, uint16_t* out, float* lse, int B, int H, int N, int A, int Nc,
+                 int n_groups, float scale_log2, const int32_t* active_idx, int ld_act,
+                 int32_t* err_count, const int32_t* a_len, const int32_t* c_len,
+                 hipStream_t stream) {
+    const int units = B * H;
+    const int grid = (n_groups == 1) ? units : ((units + 7) / 8) * 8 * n_groups;
+    static_assert(split_region(NQT, SPLIT) <= 56 * 1024, "split workgroup LDS");
+    const size_t lds = split_lds(NQT, SPLIT, UPDATE, A, Nc);  // <= 64 KB (checked by the caller)
+    if (a_len != nullptr)
+        hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, true, false, SPLIT>), dim3(grid),
+                           dim3(64 * SPLIT), lds, stream, q_a, k_a, v_a, k_cache, v_cache,
+                           cached_idx, ldc, out, lse, units, H, N, A, Nc, n_groups, scale_log2,
+                           active_idx, ld_act, err_count, a_len, c_len);
+    else
+        hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, false, false, SPLIT>), dim3(grid),
+                           dim3(64 * SPLIT), lds, stream, q_a, k_a, v_a, k_cache, v_cache,
+                           cached_idx, ldc, out, lse, units, H, N, A, Nc, n_groups, scale_log2,
+                           active_idx, ld_act, err_count, a_len, c_len);
+    return status_from_launch();
+}
+
+template <int NQT, bool UPDATE>
+int launch_maybe_split(const uint16_t* q, const uint16_t* ka, const uint16_t* va,
+                       const uint16_t* kc, const uint16_t* vc, const int32_t* cached_idx,
+                       int ldc, uint16_t* o, float* lse, int B, int H, int N, int A, int Nc,
+                       int n_groups, float scale_log2, const int32_t* active_idx, int ld_act,
+                       int32_t* err_count, const int32_t* a_len, const int32_t* c_len,
+                       hipStream_t stream) {
+    const bool dense = a_len == nullptr && Nc == 0;
+    int split = dense ? 1 : split_for(B * H, n_groups, (A + Nc + kChunk - 1) / kChunk, NQT);
+    // fewer waves when the staged lists would not fit the workgroup's 64 KB
+    while (split > 1 && split_lds(NQT, split, UPDATE, A, Nc) > 64 * 1024) split /= 2;
+    switch (split) {
+        case 2:
+            return launch_split<NQT, UPDATE, 2>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H,
+                                                N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
+                                                err_count, a_len, c_len, stream);
+        case 4:
+            return launch_split<NQT, UPDATE, 4>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H,
+                                                N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
+                                                err_count, a_len, c_len, stream);
+        case 8:
+            if constexpr (NQT < 4)
+                return launch_split<NQT, UPDATE, 8>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B,
+                                                    H, N, A, Nc, n_groups, scale_log2, active_idx,
+                                                    ld_act, err_count, a_len, c_len, stream);
+            [[fallthrough]];
+        default:
+            return launch_mfma<NQT, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N,
+                                            A, Nc, n_groups, scale_log2, active_idx, ld_act,
+                                            err_count, a_len, c_len, stream);
+    }
+}
+
 template <bool UPDATE>
 int dispatch_mfma(const uint16_t* q, const uint16_t* ka, const uint16_t* va, const uint16_t* kc,
                   const uint16_t* vc, const int32_t* cached_idx, int ldc, uint16_t* o, float* lse,
@@ -939,21 +1112,21 @@ int dispatch_mfma(const uint16_t* q, const uint16_t* ka, const uint16_t* va, con
     const int nqt = (n_groups > 1) ? 4 : (A + 15) / 16;
     switch (nqt) {
         case 1:
-            return launch_mfma<1, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
-                                          Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
-                                          a_len, c_len, stream);
+            return launch_maybe_split<1, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H,
+                                                 N, A, Nc, n_groups, scale_log2, active_idx,
+                                                 ld_act, err_count, a_len, c_len, stream);
         case 2:
-            return launch_mfma<2, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
-                                          Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
-                                          a_len, c_len, stream);
+            return launch_maybe_split<2, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H,
+                                                 N, A, Nc, n_groups, scale_log2, active_idx,
+                                                 ld_act, err_count, a_len, c_len, stream);
         case 3:
-            return launch_mfma<3, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
-                                          Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
-                                          a_len, c_len, stream);
+            return launch_maybe_split<3, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H,
+                                                 N, A, Nc, n_groups, scale_log2, active_idx,
+                                                 ld_act, err_count, a_len, c_len, stream);
         default:
-            return launch_mfma<4, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
-                                          Nc, n_groups, scale_log2, active_idx, ld_act, err_count,
-                                          a_len, c_len, stream);
+            return launch_maybe_split<4, UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H,
+                                                 N, A, Nc, n_groups, scale_log2, active_idx,
+                                                 ld_act, err_count, a_len, c_len, stream);
     }
 }
 
