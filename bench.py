@@ -173,6 +173,21 @@ def build_inputs(cfg, dev):
     return x
 
 
+SEQ_KEYS = ("gp", "q_gen", "k_full", "scores", "active_idx", "cached_idx", "cached_len",
+            "gate_x", "gate_y", "cos", "reuse", "cidx", "clen", "full_out")
+
+
+def seq_view(x, nb):
+    """The first nb sequences of every per-sequence tensor of the step (views of
+    the same memory).  The conditional branch of each image's CFG pair comes
+    first in the batch, so nb = B/2 is the conditional branch alone."""
+    v = dict(x)
+    for k in SEQ_KEYS:
+        v[k] = x[k][:nb]
+    v["layers"] = [{k: t[:nb] for k, t in L.items()} for L in x["layers"]]
+    return v
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,19 +246,26 @@ def main():
     side = torch.cuda.Stream()
     layer_done = [torch.cuda.Event() for _ in range(cfg.layers)]
     side_done = torch.cuda.Event()
+    # The sequences the step functions below run on: the whole batch, or (on a
+    # condition-cache step of the decode) its conditional half.
+    X = [x]
+    x_cond = seq_view(x, cfg.B_img)
 
     def topk(plan):
+        x = X[0]
         marca.mar_refresh_topk(x["q_gen"], x["k_full"], x["gp"], plan.n_prev + plan.n_gen,
                                plan.n_refresh, scores=x["scores"], active_idx=x["active_idx"],
                                cached_idx=x["cached_idx"], cached_len=x["cached_len"],
                                workspace=x["workspace"])
 
     def attn(l, plan):
+        x = X[0]
         L = x["layers"][l]
         marca.mar_cache_attn_fwd(L["q_a"], L["k_a"], L["v_a"], L["k_cache"], L["v_cache"],
                                  x["cached_idx"], Nc=plan.n_cached, out=L["out"])
 
     def scatter(l, on=None):
+        x = X[0]
         L = x["layers"][l]
         marca.mar_kv_scatter_refresh(L["k_cache"], L["v_cache"], L["k_a"], L["v_a"],
                                      x["active_idx"], stream=on)
@@ -261,6 +283,7 @@ def main():
         stream.wait_event(side_done)
 
     def fused(l, plan):
+        x = X[0]
         L = x["layers"][l]
         marca.mar_cache_attn_fwd_update(L["q_a"], L["k_a"], L["v_a"], L["k_cache"],
                                         L["v_cache"], x["cached_idx"], x["active_idx"],
@@ -270,6 +293,7 @@ def main():
         """A full-attention layer (layers 1-2 of every step, every layer of a
         refresh step): all N tokens active, no cached rows.  Layer l's stored
         K/V stand in for its fresh K/V and the next layer's K for its Q."""
+        x = X[0]
         L, Lq = x["layers"][l], x["layers"][(l + 1) % n_ca]
         marca.mar_cache_attn_fwd(Lq["k_cache"], L["k_cache"], L["v_cache"], L["k_cache"],
                                  L["v_cache"], None, Nc=0, out=x["full_out"])
@@ -279,6 +303,7 @@ def main():
                                uncond_out=x["uncond_out"])
 
     def gate():
+        x = X[0]
         marca.mar_cos_gate(x["gate_x"], x["gate_y"], 0.95, cos_out=x["cos"],
                            reuse_mask=x["reuse"], compute_idx=x["cidx"], compute_len=x["clen"])
 
@@ -311,17 +336,21 @@ def main():
         and the rewrite of every row of the layer's cache with the fresh K/V, in
         one call (the next layer's stored K/V stand in for the fresh K/V, the one
         after it for Q)."""
+        x = X[0]
         L, Ln, Lq = (x["layers"][(l + i) % n_ca] for i in range(3))
         marca.mar_cache_attn_fwd_update(Lq["k_cache"], Ln["k_cache"], Ln["v_cache"],
                                         L["k_cache"], L["v_cache"], None, None, Nc=0,
                                         out=x["full_out"])
 
-    def decode(use_cache):
+    def decode(use_cache, cond_cache=False):
         """A whole 64-step decode of the attention path.  With the cache: on a
         refresh step (t mod 3 = 0) every layer runs full attention and rewrites
         its cache, and the CFG residual is stored; on the other steps layers 1-2
-        run full attention and layers 3-32 run the cached step above.  Without
-        the cache every layer of every step runs full attention."""
+        run full attention and layers 3-32 run the cached step above.  With the
+        condition cache as well, those other steps compute the conditional
+        branch only (half the sequences) and take the unconditional output from
+        the stored residual.  Without the cache every layer of every step runs
+        full attention."""
         for t in range(cfg.steps):
             if not use_cache:
                 for l in range(cfg.layers):
@@ -336,12 +365,15 @@ def main():
                 marca.mar_cfg_residual(x["cond"], x["uncond_out"], residual=x["residual"],
                                        mode=marca.MAR_CFG_STORE)
                 continue
+            if cond_cache:
+                X[0] = x_cond
             full_attn(0)
             full_attn(1)
             topk(plan)
             cached_layers(plan)
             cfg_reuse()
             gate()
+            X[0] = x
 
     def timed_kernels():
         """The same launches as one step, grouped by kernel so that one pair of HIP
@@ -396,15 +428,16 @@ def main():
 
     # Timed region 1c: whole decodes, with and without the cache.
     decode_ms = {}
-    for use_cache in (() if args.no_decode else (True, False)):
-        decode(use_cache)
+    for mode in (() if args.no_decode else ("cache", "none", "cache+cond")):
+        run = lambda: decode(mode != "none", cond_cache=mode == "cache+cond")
+        run()
         torch.cuda.synchronize()
         d0, d1 = ev(), ev()
         d0.record(stream)
-        decode(use_cache)
+        run()
         d1.record(stream)
         torch.cuda.synchronize()
-        decode_ms[use_cache] = d0.elapsed_time(d1)
+        decode_ms[mode] = d0.elapsed_time(d1)
     n_refresh_steps = sum(marca.mar_plan_step(decode_counts, t, cfg.N, cfg.budget).refresh
                           for t in range(cfg.steps))
 
@@ -482,10 +515,14 @@ def main():
         "decode": None if args.no_decode else {
             "what": "one 64-step decode of the attention path (every layer's attention, cache "
                     "writes, top-K, CFG and gate; no projections or MLPs), with the cache "
-                    "(refresh every 3rd step) and without it (full attention everywhere)",
+                    "(refresh every 3rd step) and without it (full attention everywhere); "
+                    "ms_cond_cache adds the condition cache: the steps between refreshes "
+                    "compute the conditional half of the batch only",
             "steps": cfg.steps, "refresh_steps": n_refresh_steps, "layers": cfg.layers,
-            "ms": decode_ms.get(True), "ms_no_cache": decode_ms.get(False),
-            "speedup": decode_ms.get(False, 0) / decode_ms.get(True, 1)},
+            "ms": decode_ms.get("cache"), "ms_no_cache": decode_ms.get("none"),
+            "speedup": decode_ms.get("none", 0) / decode_ms.get("cache", 1),
+            "ms_cond_cache": decode_ms.get("cache+cond"),
+            "speedup_cond_cache": decode_ms.get("none", 0) / decode_ms.get("cache+cond", 1)},
         "attn_bytes_per_call": bytes_call,
         "attn_tok_per_s": cfg.B * cfg.A / (avg_us["attn"] * 1e-6),
         "copy_gbs": copy_gbs,
