@@ -5,9 +5,11 @@ error max|g - r| / max|r| <= 1e-5 per (sequence, head) tile; bf16 inputs with
 float accumulation -- max-abs error <= 2e-2 on the unit-scale outputs.  The
 log-sum-exp is compared to 1e-5 relative in fp32.  In bf16 the softmax
 denominator sums the same bf16-rounded probabilities as the numerator, so it
-carries a relative error of at most 2^-9 (bf16 unit roundoff) plus float
-accumulation (at most T * 2^-24 for T keys, below 5e-4 up to 8192 keys): the
-log-sum-exp bound is ln(1 + 2^-9) + 5e-4 < 2.5e-3 absolute.
+carries a relative error of at most 2^-8 (the unit roundoff of bf16's 8-bit
+significand) plus float accumulation (at most T * 2^-24 for T keys, below
+5e-4 up to 8192 keys): the log-sum-exp bound is ln(1 + 2^-8) + 5e-4 < 4.5e-3
+absolute.  A nearly one-hot softmax comes close to it: its one dominant
+probability carries the whole rounding error.
 """
 import numpy as np
 import pytest
@@ -56,7 +58,7 @@ def check(got_out, got_lse, ref_out, ref_lse, dtype):
     else:
         err = np.abs(got_out - ref_out).max()
         assert err <= 2e-2, f"max-abs error {err}"
-        assert np.abs(got_lse - ref_lse).max() <= 2.5e-3
+        assert np.abs(got_lse - ref_lse).max() <= 4.5e-3
 
 
 def run(marca, x, Nc=None, cached=None):

@@ -38,7 +38,7 @@ def small_cfg(B, H, N, A, seed):
                   dtype="bf16", stale=True, seed=seed)
 
 
-def attn_vs_oracle(marca, x, Nc, cached, units, lse_tol=2.5e-3):
+def attn_vs_oracle(marca, x, Nc, cached, units, lse_tol=4.5e-3):
     import oracle
     B, H, A, D = x["q_a"].shape
     lse = torch.empty((B, H, A), dtype=torch.float32, device=DEV)
@@ -165,4 +165,4 @@ def test_full_attention_long_and_partial_blocks(marca, B, H, N, update):
         o, l = oracle.cache_attention(sl(q), sl(k), sl(v), sl(k), sl(v),
                                       np.zeros((1, 1), np.int32), D ** -0.5, Nc=0)
         assert np.abs(f64(out[b, h]) - o[0, 0]).max() <= 2e-2
-        assert np.abs(f64(lse[b, h]) - l[0, 0]).max() <= 2.5e-3
+        assert np.abs(f64(lse[b, h]) - l[0, 0]).max() <= 4.5e-3

@@ -68,7 +68,7 @@ def test_ragged_lengths(marca, dtype, A, Nc):
             got = f64(out[b, h, :an])
             if dtype == "bf16":
                 assert np.abs(got - o).max() <= 2e-2, (b, h)
-                assert np.abs(f64(lse[b, h, :an]) - l).max() <= 2.5e-3
+                assert np.abs(f64(lse[b, h, :an]) - l).max() <= 4.5e-3
             else:
                 assert np.abs(got - o).max() / np.abs(o).max() <= 1e-5, (b, h)
 

@@ -1,0 +1,105 @@
+"""GPU parity when the online softmax has to rescale after its first chunk.
+
+The kernels keep a reference maximum per query and rescale their (max, sum,
+weighted sum) state only when a score exceeds it by more than 2^8 in base 2;
+with N(0, 1) inputs that rarely happens after the first chunk.  Here key row j
+is scaled by 1 + 3 j / N (and, in the cached case, the cached rows after the
+active ones grow further), so each query's maximum climbs many times along
+the sequence and every kernel takes its rescale path repeatedly:
+
+* the full-attention workgroup kernel (A = N > 64, no cached rows), with and
+  without the refresh-step cache rewrite;
+* the one-wave cache-aware kernel (48 active queries, 272 cached rows), at
+  many units (one wave per unit) and at few units (several waves per unit,
+  merged at the end), and fused with the cache update.
+
+Every listed unit is checked against the oracle: bf16 max-abs 2e-2 on the
+outputs, 4.5e-3 on the log-sum-exp (the same bounds as elsewhere: the
+denominator sums the same bf16-rounded probabilities as the numerator, each
+with a relative error of at most 2^-8, so the log-sum-exp is within
+ln(1 + 2^-8) + 5e-4; these peaked softmaxes come close to that bound).
+"""
+import numpy as np
+import pytest
+import torch
+
+from mar_workloads import device_normal
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+@pytest.fixture(scope="module")
+def marca():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import cache_aware_attention_amd as m
+    return m
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def ramp(n, top=3.0):
+    return (1.0 + top * torch.arange(n, dtype=torch.float32, device=DEV) / n)[None, None, :, None]
+
+
+def check(q, ka, va, kc, vc, cached, Nc, out, lse, units):
+    import oracle
+    cl = cached.cpu().numpy() if cached is not None else np.zeros((q.shape[0], 1), np.int32)
+    for b, h in units:
+        sl = lambda t: f64(t[b:b + 1, h:h + 1])
+        o, l = oracle.cache_attention(sl(q), sl(ka), sl(va), sl(kc), sl(vc), cl[b:b + 1],
+                                      q.shape[-1] ** -0.5, Nc=Nc)
+        assert np.abs(f64(out[b, h]) - o[0, 0]).max() <= 2e-2, (b, h)
+        assert np.abs(f64(lse[b, h]) - l[0, 0]).max() <= 4.5e-3, (b, h)
+
+
+@pytest.mark.parametrize("B,H,N", [(4, 4, 320), (2, 2, 1088)])
+def test_full_attention_rising_scores(marca, B, H, N):
+    q, k, v = (device_normal((B, H, N, 64), 900 + N + i, DEV, torch.bfloat16) for i in range(3))
+    q = (q.float() * 2.0).to(torch.bfloat16)
+    k = (k.float() * ramp(N) * 2.0).to(torch.bfloat16)
+    # scores of the last keys exceed those of the first chunk by far more than 2^8
+    s = (q[0, 0].float() @ k[0, 0].float().t()) / 8.0
+    assert (s[:, -32:].max(1).values - s[:, :32].max(1).values).max() * 1.4427 > 16
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    out = marca.mar_cache_attn_fwd(q, k, v, k, v, None, Nc=0, lse=lse)
+    kc, vc = torch.zeros_like(k), torch.zeros_like(v)
+    lse2 = torch.empty_like(lse)
+    out2 = marca.mar_cache_attn_fwd_update(q, k, v, kc, vc, None, None, Nc=0, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
+    assert torch.equal(kc, k) and torch.equal(vc, v)
+    check(q, k, v, k, v, None, 0, out, lse, [(0, 0), (B - 1, H - 1), (B // 2, 1)])
+
+
+@pytest.mark.parametrize("B,H", [(40, 8), (2, 2)])  # one wave per unit / several waves per unit
+def test_cache_aware_rising_scores(marca, B, H):
+    N, A, Nc = 320, 48, 272
+    q, ka, va = (device_normal((B, H, A, 64), 950 + i, DEV, torch.bfloat16) for i in range(3))
+    kc, vc = (device_normal((B, H, N, 64), 960 + i, DEV, torch.bfloat16) for i in range(2))
+    q = (q.float() * 2.0).to(torch.bfloat16)
+    ka = (ka.float() * 2.0).to(torch.bfloat16)
+    # cached token n's row grows with n; the list walks the tokens in ascending order
+    kc = (kc.float() * ramp(N) * 2.0).to(torch.bfloat16)
+    s = (q[0, 0].float() @ kc[0, 0].float().t()) / 8.0
+    assert (s[:, -32:].max(1).values - s[:, :32].max(1).values).max() * 1.4427 > 16
+    g = torch.Generator().manual_seed(B)
+    cached = torch.stack([torch.sort(torch.randperm(N, generator=g)[:Nc]).values
+                          for _ in range(B)]).to(torch.int32).to(DEV)
+    lse = torch.empty((B, H, A), dtype=torch.float32, device=DEV)
+    out = marca.mar_cache_attn_fwd(q, ka, va, kc, vc, cached, Nc=Nc, lse=lse)
+    torch.cuda.synchronize()
+    check(q, ka, va, kc, vc, cached, Nc, out, lse, [(0, 0), (B - 1, H - 1), (B // 2, 1)])
+
+    # fused with the cache update of the active rows: same bits
+    active = torch.stack([torch.tensor(sorted(set(range(N)) - set(c.tolist()))[:A])
+                          for c in cached.cpu()]).to(torch.int32).to(DEV)
+    kc2, vc2 = kc.clone(), vc.clone()
+    lse2 = torch.empty_like(lse)
+    out2 = marca.mar_cache_attn_fwd_update(q, ka, va, kc2, vc2, cached, active, Nc=Nc, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)

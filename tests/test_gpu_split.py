@@ -7,12 +7,12 @@ wave.
 Each case runs the same two sequences twice: alone (2 sequences x 2 heads, so
 the unit is split over waves) and tiled into a batch of 160 sequences (320
 units: one wave per unit).  Both results are checked against the oracle
-(bf16: max-abs 2e-2, log-sum-exp 2.5e-3), and against each other.  The
-kernel rounds the softmax probabilities to bf16 (relative error at most 2^-9)
+(bf16: max-abs 2e-2, log-sum-exp 4.5e-3), and against each other.  The
+kernel rounds the softmax probabilities to bf16 (relative error at most 2^-8)
 relative to each wave's own running maximum, so the two schedules round them
 differently; the denominator sums the same rounded values, so each output
-element is within 2^-8 * sum_i w_i |v_i| of the exact one (w: the softmax
-weights), and the two differ by at most 2^-7 * sum_i w_i |v_i| plus one bf16
+element is within 2^-7 * sum_i w_i |v_i| of the exact one (w: the softmax
+weights), and the two differ by at most 2^-6 * sum_i w_i |v_i| plus one bf16
 unit in the last place of the output.  sum_i w_i |v_i| is the oracle's
 attention with |V| as the values.
 
@@ -92,11 +92,11 @@ def oracle_check(ts, cached, out, lse, an=None, cn=None):
             err = np.abs(f64(out[b, h, :a_b]) - o[0, 0]).max()
             assert err <= 2e-2, f"unit ({b},{h}): max-abs {err}"
             if lse is not None:
-                assert np.abs(f64(lse[b, h, :a_b]) - l[0, 0]).max() <= 2.5e-3, (b, h)
+                assert np.abs(f64(lse[b, h, :a_b]) - l[0, 0]).max() <= 4.5e-3, (b, h)
             wabs, _ = oracle.cache_attention(args[0], args[1], np.abs(args[2]), args[3],
                                              np.abs(args[4]), cl[b:b + 1, :max(c_b, 1)], 0.125,
                                              Nc=c_b)
-            bound[b, h, :a_b] = 2.0 ** -7 * wabs[0, 0]
+            bound[b, h, :a_b] = 2.0 ** -6 * wabs[0, 0]
     return bound
 
 
@@ -124,8 +124,8 @@ def test_split_matches_one_wave_and_oracle(marca, N, A, Nc):
     for t in range(TILE):  # every copy in the big batch computes the same thing
         assert torch.equal(big_out[2 * t:2 * t + 2], big_out[:2])
     close_schedules(out, big_out[:2], bound)
-    # the denominators differ by the same rounding: |log(1 + 2^-8)| < 4e-3 each way
-    np.testing.assert_allclose(f64(lse), f64(big_lse[:2]), rtol=0, atol=8e-3)
+    # each log-sum-exp is within 4.5e-3 of the exact one
+    np.testing.assert_allclose(f64(lse), f64(big_lse[:2]), rtol=0, atol=9e-3)
 
 
 @pytest.mark.parametrize("N,A,Nc", [CASES[0], CASES[1], CASES[3]])

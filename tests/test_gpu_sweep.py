@@ -7,7 +7,7 @@ tiles and one or several query groups, the dense workgroup kernel with full
 and partial last chunks and partly idle workgroups, the row-wise path (A < 16),
 empty and all-invalid cached lists, the fused cache update with a list and the
 full refresh without one, and per-sequence counts.  Tolerances as everywhere:
-bf16 max-abs 2e-2 (lse 2.5e-3), fp32 normwise 1e-5.
+bf16 max-abs 2e-2 (lse 4.5e-3), fp32 normwise 1e-5.
 """
 import numpy as np
 import pytest
@@ -87,7 +87,7 @@ def oracle_units(q, ka, va, kc, vc, cached, Nc, out, lse, an=None, cn=None, tol=
             if q.dtype == torch.bfloat16:
                 assert np.abs(got - o[0, 0]).max() <= tol, (b, h)
                 if lse is not None:
-                    assert np.abs(f64(lse[b, h, :a_b]) - l[0, 0]).max() <= 2.5e-3, (b, h)
+                    assert np.abs(f64(lse[b, h, :a_b]) - l[0, 0]).max() <= 4.5e-3, (b, h)
             else:
                 assert np.abs(got - o[0, 0]).max() / np.abs(o[0, 0]).max() <= 1e-5, (b, h)
 
