@@ -23,7 +23,8 @@
 //    contiguous rows read at fixed per-lane offsets.
 //  * attn_dense_wg_kernel (bf16, no cached rows, A > 64: the full-attention
 //    layers): a 4-wave workgroup per 320 queries of a unit shares each K/V
-//    chunk through a double-buffered LDS tile; same per-tile arithmetic.
+//    chunk through a double-buffered LDS tile; the same MFMA tiles, with the
+//    softmax reference kept in scaled units and the query tiles in pairs.
 //  * attn_rowwise_kernel (fp32 any A, bf16 A < 16): one wave per query, one
 //    lane per head-dim element; plain FMA.  Exact-precision path for fp32.
 //
@@ -711,9 +712,17 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 // MFMA operands from there.  A unit's K/V then crosses the L2-to-CU path once
 // per workgroup instead of once per 64-query wave, which is what bounds the
 // one-wave kernel at these sizes.  With UPDATE the loading lanes also write
-// their pieces into the caches (row r to cache row r).  The arithmetic per
-// 16-query tile is that of attn_mfma_kernel, chunk for chunk, so both give
-// the same bits.
+// their pieces into the caches (row r to cache row r).
+// The MFMA tiles are those of attn_mfma_kernel.  The softmax state differs:
+//  * each query keeps one reference mc, a maximum of its scaled scores
+//    s * scale_log2, set from the first chunk (a full one, since A > 64);
+//  * a tile computes x = s * scale_log2 - mc first and tests max(x) against
+//    kRescaleLog2 (an inline constant), so no raw maximum or threshold has
+//    to stay in registers;
+//  * the query tiles go in pairs under one rescale test, so both tiles'
+//    exponentials and conversions sit in one basic block and interleave.
+// The first chunk sets the same reference in both kernels, so a unit that
+// needs no later rescale gets the same bits from both.
 // ---------------------------------------------------------------------------
 constexpr int kWgWaves = 4;
 constexpr int kWgNqt = 5;
@@ -811,13 +820,12 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
         kofs[t][1] = swz(16 * t + m16, 4 + g);
     }
 
-    const float thr_raw = kRescaleLog2 / scale_log2;
-    float mref[NQT], mc[NQT], mthr[NQT];
+    // mc: the reference maximum of each query's scaled scores s * scale_log2
+    // (set from the first chunk, which has no row past A since A > 64).
+    float mc[NQT];
     f32x4_t oacc[NQT][4], lacc[NQT];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-        mref[qt] = -INFINITY;
-        mthr[qt] = -INFINITY;
         mc[qt] = 0.f;
         lacc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -825,8 +833,9 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
     }
     const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
-    auto compute = [&](int c, int buf, auto full_tag) __attribute__((always_inline)) {
+    auto compute = [&](int c, int buf, auto full_tag, auto first_tag) __attribute__((always_inline)) {
         constexpr bool kFull = decltype(full_tag)::value;  // no row of the chunk past A
+        constexpr bool kFirst = decltype(first_tag)::value;  // chunk 0: sets the references
         const unsigned char* kt = lds + buf * 2 * kWgTile;
         const unsigned char* vt = kt + kWgTile;
         uint4 kop[2][2];
@@ -843,9 +852,7 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
             va[dt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
         const int r0 = c * kChunk;
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            if (qt * 16 >= nq) continue;  // wave-uniform
+        auto scores = [&](int qt, float (&x)[8]) __attribute__((always_inline)) {
             f32x4_t s[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -863,28 +870,38 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
                     for (int i = 0; i < 4; ++i)
                         if (r0 + 16 * t + 4 * g + i >= A) s[t][i] = -INFINITY;
             }
-            const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-            // A query's maximum moved far up: rescale (rare; kept off the
-            // straight-line path so it is not turned into selects).
-            if (__builtin_expect(__any(mx > mthr[qt]), 0)) {
-                const float mnew = fmaxf(mref[qt], max_over_groups(mx));
-                const float alpha = (mref[qt] == -INFINITY)
-                                        ? 0.f
-                                        : __builtin_amdgcn_exp2f((mref[qt] - mnew) * scale_log2);
-                lacc[qt] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] *= alpha;
-                mref[qt] = mnew;
-                mc[qt] = mnew * scale_log2;
-                mthr[qt] = mnew + thr_raw;
+            if constexpr (kFirst) {
+                const float m1 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+                const float m2 = fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]);
+                const float ms = fmaxf(fmaxf(s[1][2], s[1][3]), fmaxf(m1, m2));
+                mc[qt] = max_over_groups(ms) * scale_log2;
             }
-            float p[8];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    p[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(s[t][i], scale_log2, -mc[qt]));
+                for (int i = 0; i < 4; ++i) x[4 * t + i] = fmaf(s[t][i], scale_log2, -mc[qt]);
+        };
+        auto xmax = [&](const float (&x)[8]) __attribute__((always_inline)) {
+            const float m1 = fmaxf(fmaxf(x[0], x[1]), x[2]);
+            const float m2 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+            return fmaxf(fmaxf(x[6], x[7]), fmaxf(m1, m2));
+        };
+        auto rescale = [&](int qt, float mx, float (&x)[8]) __attribute__((always_inline)) {
+            const float up = max_over_groups(mx);
+            if (up > kRescaleLog2) {
+                const float alpha = __builtin_amdgcn_exp2f(-up);
+                lacc[qt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] *= alpha;
+                mc[qt] += up;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] -= up;
+            }
+        };
+        auto finish = [&](int qt, const float (&x)[8]) __attribute__((always_inline)) {
+            float p[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(x[i]);
             U4 pk;
             pk.u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
@@ -893,6 +910,34 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
             for (int dt = 0; dt < 4; ++dt)
                 oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk.v,
                                                                        oacc[qt][dt], 0, 0, 0);
+        };
+        // Query tiles in pairs: both tiles' chains sit in one basic block
+        // (one rescale test per pair), so their instructions interleave.
+#pragma unroll
+        for (int qt = 0; qt < NQT; qt += 2) {
+            if (qt * 16 >= nq) continue;  // wave-uniform
+            if (qt + 1 < NQT) {
+                float x0[8], x1[8];
+                scores(qt, x0);
+                scores(qt + 1, x1);
+                if constexpr (!kFirst) {
+                    const float m0 = xmax(x0), m1 = xmax(x1);
+                    if (__builtin_expect(__any(fmaxf(m0, m1) > kRescaleLog2), 0)) {
+                        rescale(qt, m0, x0);
+                        rescale(qt + 1, m1, x1);
+                    }
+                }
+                finish(qt, x0);
+                finish(qt + 1, x1);
+            } else {
+                float x0[8];
+                scores(qt, x0);
+                if constexpr (!kFirst) {
+                    const float m0 = xmax(x0);
+                    if (__builtin_expect(__any(m0 > kRescaleLog2), 0)) rescale(qt, m0, x0);
+                }
+                finish(qt, x0);
+            }
         }
     };
 
@@ -906,10 +951,10 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
     load(0, sk, sv);
     put(0, 0, sk, sv);
     __syncthreads();
-    auto step = [&](int c, auto buf_tag, auto full_tag) __attribute__((always_inline)) {
+    auto step = [&](int c, auto buf_tag, auto full_tag, auto first_tag) __attribute__((always_inline)) {
         constexpr int BI = decltype(buf_tag)::value;
         load(min(c + 1, nchunks - 1), sk, sv);
-        if (nq > 0) compute(c, BI, full_tag);
+        if (nq > 0) compute(c, BI, full_tag, first_tag);
         put(BI ^ 1, c + 1, sk, sv);
         __syncthreads();
     };
@@ -918,18 +963,21 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
     // one carries the masking.
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    const int nfull = A / kChunk;
-    int c = 0;
+    using T = std::true_type;
+    using F = std::false_type;
+    const int nfull = A / kChunk;  // >= 2 (A > 64)
+    step(0, B0{}, T{}, T{});
+    int c = 1;
     for (; c + 1 < nfull; c += 2) {
-        step(c, B0{}, std::true_type{});
-        step(c + 1, B1{}, std::true_type{});
+        step(c, B1{}, T{}, F{});
+        step(c + 1, B0{}, T{}, F{});
     }
-    if (c < nfull) step(c++, B0{}, std::true_type{});
+    if (c < nfull) step(c++, B1{}, T{}, F{});
     if (c < nchunks) {
         if (c & 1)
-            step(c, B1{}, std::false_type{});
+            step(c, B1{}, F{}, F{});
         else
-            step(c, B0{}, std::false_type{});
+            step(c, B0{}, F{}, F{});
     }
 
     // Finalise through this wave's 2 KB of the (now free) LDS tiles, one
