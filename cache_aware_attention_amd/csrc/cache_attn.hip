@@ -21,10 +21,11 @@
 //    staged in LDS once.  Separate instantiations serve per-sequence counts,
 //    the fused cache update, and the case with no cached rows, whose keys are
 //    contiguous rows read at fixed per-lane offsets.
-//  * attn_dense_wg_kernel (bf16, no cached rows, A > 64: the full-attention
-//    layers): a 4-wave workgroup per 320 queries of a unit shares each K/V
-//    chunk through a double-buffered LDS tile; the same MFMA tiles, with the
-//    softmax reference kept in scaled units and the query tiles in pairs.
+//  * attn_wg_kernel (bf16, A > 64): a workgroup per unit (per block of its
+//    queries) shares each K/V chunk through a double-buffered LDS tile among
+//    its waves -- 4 waves x 80 queries without cached rows (the full-attention
+//    layers), 2 or 4 waves x 64 queries with them; the same MFMA tiles, with
+//    the softmax reference kept in scaled units and the query tiles in pairs.
 //  * attn_rowwise_kernel (fp32 any A, bf16 A < 16): one wave per query, one
 //    lane per head-dim element; plain FMA.  Exact-precision path for fp32.
 //
@@ -703,19 +704,30 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Dense workgroup kernel: all tokens active and no cached rows (the
-// full-attention layers, and with UPDATE a refresh step's layer).  One
-// workgroup of kWgWaves waves per (unit, block of kWgWaves * 16 * NQT
-// queries); NQT = 5 makes one workgroup cover a 320-token unit.  Each 32-row
-// K/V chunk is loaded once per workgroup -- every lane one 16-byte piece of K
-// and one of V -- into a double-buffered LDS tile, and every wave reads its
-// MFMA operands from there.  A unit's K/V then crosses the L2-to-CU path once
-// per workgroup instead of once per 64-query wave, which is what bounds the
-// one-wave kernel at these sizes.  With UPDATE the loading lanes also write
-// their pieces into the caches (row r to cache row r).
+// Workgroup kernel: more queries per unit than one wave holds (A > 64).  One
+// workgroup of W waves per (unit, block of W * 16 * NQT queries).  Each 32-row
+// K/V chunk of the unit's sequence is loaded once per workgroup into a
+// double-buffered LDS tile, and every wave reads its MFMA operands from there.
+// A unit's K/V then crosses the L2-to-CU path once per workgroup instead of
+// once per 64-query wave, which is what bounds the one-wave kernel once a unit
+// has several query groups.
+//  * CACHED = false (no cached rows: the full-attention layers, W = 4, NQT = 5
+//    so that one workgroup covers a 320-token unit): the keys are rows 0..A-1
+//    of k_a/v_a, read with range-checked buffer loads (a row past A reads as
+//    zero and is masked).  With UPDATE the loading lanes also write their
+//    pieces into the caches, row r to cache row r (a refresh step's layer);
+//    block c mod n_blocks writes chunk c.
+//  * CACHED = true (the cache-aware layers with several query groups, W = 2
+//    or 4, NQT = 4): the sequence is [the A active rows ; the Nc cached rows
+//    at the staged list's token positions].  The list is staged in LDS once
+//    (entries outside [0, N) become -1) together with one flag per chunk that
+//    says whether every row of the chunk exists; only chunks without that
+//    flag carry the masking.  With UPDATE the loading lanes of the unit's
+//    first block write the active rows into the caches at active_idx.
 // The MFMA tiles are those of attn_mfma_kernel.  The softmax state differs:
 //  * each query keeps one reference mc, a maximum of its scaled scores
-//    s * scale_log2, set from the first chunk (a full one, since A > 64);
+//    s * scale_log2, set from the first chunk (A > 64 active rows, so the
+//    first chunk is always complete);
 //  * a tile computes x = s * scale_log2 - mc first and tests max(x) against
 //    kRescaleLog2 (an inline constant), so no raw maximum or threshold has
 //    to stay in registers;
@@ -728,15 +740,22 @@ constexpr int kWgWaves = 4;
 constexpr int kWgNqt = 5;
 constexpr int kWgTile = kChunk * 128;  // bytes of one K or V chunk tile
 
-template <int NQT, bool UPDATE>
-__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
-void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
-                          const uint16_t* __restrict__ v_a, uint16_t* k_cache, uint16_t* v_cache,
-                          uint16_t* __restrict__ out, float* __restrict__ lse, int units, int A,
-                          int n_blocks, float scale_log2) {
-    constexpr int kQ = 16 * NQT;  // queries per wave
+template <int NQT, int W, bool UPDATE, bool CACHED>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
+                    const uint16_t* __restrict__ v_a, uint16_t* k_cache, uint16_t* v_cache,
+                    uint16_t* __restrict__ out, float* __restrict__ lse, int units, int A,
+                    int n_blocks, float scale_log2, const int32_t* __restrict__ cached_idx,
+                    int ldc, int H, int N, int Nc, const int32_t* __restrict__ active_idx,
+                    int ld_act, int32_t* __restrict__ err_count) {
+    static_assert(W == 1 || W == 2 || W == 4, "waves per workgroup");
+    constexpr int kQ = 16 * NQT;         // queries per wave
+    constexpr int kPasses = 4 / W;       // load passes per chunk (8 W rows each)
     __shared__ __align__(16) unsigned char lds[4 * kWgTile];  // 2 buffers x (K tile, V tile)
-    static_assert(4 * kWgTile >= kWgWaves * 2048, "the output staging reuses the K/V tiles");
+    static_assert(4 * kWgTile >= W * 2048, "the output staging reuses the K/V tiles");
+    // CACHED: the staged lists after the tiles, [max(Nc, 1)] entries, the
+    // chunk flags [nchunks], and with UPDATE the active positions [A].
+    extern __shared__ __align__(16) int32_t wg_lists[];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -754,43 +773,87 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
         qb = slot % n_blocks;
         if (u >= units) return;  // uniform over the workgroup, before any barrier
     }
-    const int q0 = (qb * kWgWaves + w) * kQ;
+    const int q0 = (qb * W + w) * kQ;
     const int nq = min(A - q0, kQ);  // <= 0: the wave loads and waits, computes nothing
     const size_t ub = static_cast<size_t>(u) * A * kD;
-    const int nchunks = (A + kChunk - 1) / kChunk;
+    // CACHED: the active rows fill chunks [0, na) (the last one padded), the
+    // cached rows start on the next chunk: row A0 + j is cached entry j.
+    const int na = (A + kChunk - 1) / kChunk;
+    const int A0 = CACHED ? na * kChunk : A;
+    const int T = CACHED ? A0 + Nc : A;  // rows of the unit's (padded) sequence
+    const int nchunks = (T + kChunk - 1) / kChunk;
     const __amdgpu_buffer_rsrc_t rka = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(k_a + ub), 0, A * kD * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rva = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(v_a + ub), 0, A * kD * 2, 0x00020000);
+    const size_t cb = static_cast<size_t>(u) * N * kD;  // the unit's cache rows (CACHED)
 
-    // Loading lane: piece tid % 8 of row tid / 8 of the chunk, for K and V.
-    // A row past A reads as zero (range-checked buffer load).
+    int32_t* cidx_s = wg_lists;                       // [max(Nc, 1)]
+    int32_t* cflag_s = cidx_s + (Nc > 0 ? Nc : 1);    // [nchunks]
+    int32_t* aidx_s = cflag_s + nchunks;              // [A] with UPDATE
+    // Loading lane: piece tid % 8 of rows 8 W p + tid / 8 (p < kPasses) of the
+    // chunk, for K and V, by range-checked buffer loads (an offset past the
+    // buffer reads as zero).  A row past A (no cached rows), a skipped cached
+    // entry or a row past the sequence reads as zero and is masked.
     const int lrow = tid >> 3;
-    const int gofs = lrow * (kD * 2) + 16 * (tid & 7);
-    const int lofs = swz(lrow, tid & 7);
-    auto load = [&](int c, uint4& kk, uint4& vv) __attribute__((always_inline)) {
-        const int rb = c * kChunk * (kD * 2);
-        kk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rka, rb + gofs, 0, 0));
-        vv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rva, rb + gofs, 0, 0));
+    const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(k_cache + (CACHED ? cb : 0)), 0, CACHED ? N * kD * 2 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(v_cache + (CACHED ? cb : 0)), 0, CACHED ? N * kD * 2 : 0, 0x00020000);
+    auto load = [&](int c, uint4 (&kk)[kPasses], uint4 (&vv)[kPasses]) __attribute__((always_inline)) {
+        constexpr uint32_t kOut = 0x80000000u;  // past any buffer: reads as zero
+        auto ld = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t ofs) __attribute__((always_inline)) {
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, ofs, 0, 0));
+        };
+        const int r0 = c * kChunk;
+        const uint32_t piece = 16 * (tid & 7);
+        if (!CACHED || r0 < A) {  // active rows (uniform; a row past A reads as zero)
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const uint32_t ofs = static_cast<uint32_t>(r0 + 8 * W * p + lrow) * (kD * 2) + piece;
+                kk[p] = ld(rka, ofs);
+                vv[p] = ld(rva, ofs);
+            }
+        } else {  // cached rows at the staged positions (the index read is in bounds)
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const int j = r0 - A0 + 8 * W * p + lrow;
+                const int n = cidx_s[min(j, Nc - 1)];
+                const uint32_t ofs = (j < Nc && n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) + piece : kOut;
+                kk[p] = ld(rkc, ofs);
+                vv[p] = ld(rvc, ofs);
+            }
+        }
     };
-    auto put = [&](int buf, int c, const uint4& kk, const uint4& vv) __attribute__((always_inline)) {
-        *reinterpret_cast<uint4*>(lds + buf * 2 * kWgTile + lofs) = kk;
-        *reinterpret_cast<uint4*>(lds + buf * 2 * kWgTile + kWgTile + lofs) = vv;
+    auto put = [&](int buf, int c, const uint4 (&kk)[kPasses], const uint4 (&vv)[kPasses]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            const int lofs = swz(8 * W * p + lrow, tid & 7);
+            *reinterpret_cast<uint4*>(lds + buf * 2 * kWgTile + lofs) = kk[p];
+            *reinterpret_cast<uint4*>(lds + buf * 2 * kWgTile + kWgTile + lofs) = vv[p];
+        }
         if constexpr (UPDATE) {
-            // A row past A, or the repeated last chunk (c >= nchunks), gets an
-            // offset past the buffer: the range check drops the store.
+            // The row's target cache row, or an offset past the buffer, which
+            // the range check drops: a row past A, a skipped entry, the
+            // repeated last chunk (c >= nchunks), a chunk another block writes.
             constexpr uint32_t kSkip = 0x80000000u;
             constexpr int kNT = 2;  // nontemporal (streaming) store
-            const int r = c * kChunk + lrow;
-            const uint32_t off = (c < nchunks && r < A)
-                                     ? static_cast<uint32_t>(c * kChunk * (kD * 2) + gofs)
-                                     : kSkip;
+            const int rows = CACHED ? N : A;
             const __amdgpu_buffer_rsrc_t rk =
-                __builtin_amdgcn_make_buffer_rsrc(k_cache + ub, 0, A * kD * 2, 0x00020000);
+                __builtin_amdgcn_make_buffer_rsrc(k_cache + (CACHED ? cb : ub), 0, rows * kD * 2, 0x00020000);
             const __amdgpu_buffer_rsrc_t rv =
-                __builtin_amdgcn_make_buffer_rsrc(v_cache + ub, 0, A * kD * 2, 0x00020000);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, kk), rk, off, 0, kNT);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vv), rv, off, 0, kNT);
+                __builtin_amdgcn_make_buffer_rsrc(v_cache + (CACHED ? cb : ub), 0, rows * kD * 2, 0x00020000);
+            if (CACHED ? (c * kChunk < A) : (c < nchunks && c % n_blocks == qb)) {  // uniform
+#pragma unroll
+                for (int p = 0; p < kPasses; ++p) {
+                    const int r = c * kChunk + 8 * W * p + lrow;
+                    const int n = (r >= A) ? -1 : (CACHED ? aidx_s[r] : r);
+                    const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) + 16 * (tid & 7)
+                                                  : kSkip;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, kk[p]), rk, off, 0, kNT);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vv[p]), rv, off, 0, kNT);
+                }
+            }
         }
     };
 
@@ -821,7 +884,7 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
     }
 
     // mc: the reference maximum of each query's scaled scores s * scale_log2
-    // (set from the first chunk, which has no row past A since A > 64).
+    // (set from the first chunk, which is complete since A > 64).
     float mc[NQT];
     f32x4_t oacc[NQT][4], lacc[NQT];
 #pragma unroll
@@ -833,8 +896,8 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
     }
     const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
-    auto compute = [&](int c, int buf, auto full_tag, auto first_tag) __attribute__((always_inline)) {
-        constexpr bool kFull = decltype(full_tag)::value;  // no row of the chunk past A
+    auto compute = [&](int c, int buf, uint32_t rows, auto full_tag, auto first_tag) __attribute__((always_inline)) {
+        constexpr bool kFull = decltype(full_tag)::value;    // every row of the chunk exists
         constexpr bool kFirst = decltype(first_tag)::value;  // chunk 0: sets the references
         const unsigned char* kt = lds + buf * 2 * kWgTile;
         const unsigned char* vt = kt + kWgTile;
@@ -852,23 +915,47 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
             va[dt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
         const int r0 = c * kChunk;
+        // CACHED: the score MFMAs start from 0 for a key row that exists and
+        // from -inf for one that does not (rows: the chunk's row mask), so
+        // every chunk takes the same path.  Otherwise (no cached rows) only
+        // the partial last chunk masks, here: the lane's key rows 16t + 4g + i
+        // that exist, at bits 16t + i.
+        f32x4_t bias[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        if constexpr (CACHED) {
+            const uint32_t have = rows >> (4 * g);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    bias[t][i] = ((have >> (16 * t + i)) & 1u) ? 0.f : -INFINITY;
+        }
+        uint32_t have = 0;
+        if constexpr (!kFull && !CACHED) {
+            {
+                const int left = A - r0 - 4 * g;  // rows past A do not exist
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) have |= (16 * t + i < left ? 1u : 0u) << (16 * t + i);
+            }
+        }
         auto scores = [&](int qt, float (&x)[8]) __attribute__((always_inline)) {
             f32x4_t s[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4_t acc = CACHED ? bias[t] : f32x4_t{0.f, 0.f, 0.f, 0.f};
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[t][0]), qf[qt][0], acc,
                                                               0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[t][1]), qf[qt][1], acc,
                                                               0, 0, 0);
                 s[t] = acc;
             }
-            if constexpr (!kFull) {
+            if constexpr (!kFull && !CACHED) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (r0 + 16 * t + 4 * g + i >= A) s[t][i] = -INFINITY;
+                        if (!((have >> (16 * t + i)) & 1u)) s[t][i] = -INFINITY;
             }
             if constexpr (kFirst) {
                 const float m1 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
@@ -886,6 +973,8 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
             const float m2 = fmaxf(fmaxf(x[3], x[4]), x[5]);
             return fmaxf(fmaxf(x[6], x[7]), fmaxf(m1, m2));
         };
+        // A query's maximum moved far up: rescale (rare; kept off the
+        // straight-line path so it is not turned into selects).
         auto rescale = [&](int qt, float mx, float (&x)[8]) __attribute__((always_inline)) {
             const float up = max_over_groups(mx);
             if (up > kRescaleLog2) {
@@ -947,37 +1036,101 @@ void attn_dense_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __re
     // barrier) and waits at the barrier.  Every step issues the same loads
     // (past the end the last chunk is requested again and not used), so the
     // compiler's memory-counter waits stay exact.
-    uint4 sk, sv;
-    load(0, sk, sv);
+    uint4 sk[kPasses], sv[kPasses];
+    load(0, sk, sv);  // chunk 0 holds active rows only (A > 64): no list needed
+    if constexpr (CACHED) {
+        // Stage the cached list (entries outside [0, N) become -1); the first
+        // kStage entries per thread are requested together.
+        const int b = u / H;
+        const int32_t* cg = cached_idx + static_cast<size_t>(b) * ldc;
+        constexpr int kStage = 8;
+        int32_t iv[kStage];
+#pragma unroll
+        for (int k = 0; k < kStage; ++k) {
+            const int c = tid + 64 * W * k;
+            iv[k] = (c < Nc) ? cg[c] : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < kStage; ++k) {
+            const int c = tid + 64 * W * k;
+            if (c < Nc) cidx_s[c] = (iv[k] >= 0 && iv[k] < N) ? iv[k] : -1;
+        }
+        for (int c = tid + 64 * W * kStage; c < Nc; c += 64 * W) {
+            const int n = cg[c];
+            cidx_s[c] = (n >= 0 && n < N) ? n : -1;
+        }
+        if constexpr (UPDATE) {
+            // Only the unit's first block writes the active rows; an entry
+            // outside [0, N) is skipped and, once per sequence, counted.
+            const int32_t* ag = active_idx + static_cast<size_t>(b) * ld_act;
+            for (int r = tid; r < A; r += 64 * W) {
+                const int n = ag[r];
+                const bool ok = n >= 0 && n < N;
+                aidx_s[r] = (ok && qb == 0) ? n : -1;
+                if (!ok && err_count != nullptr && qb == 0 && u % H == 0) atomicAdd(err_count, 1);
+            }
+        }
+        __syncthreads();
+        // Chunk c's row mask, bit k set when row 32c + k exists: one ballot
+        // per 64 rows (the index read is in bounds for every lane).
+        for (int base = 64 * w; base < nchunks * kChunk; base += 64 * W) {
+            const int r = base + lane;
+            const int n = cidx_s[min(max(r - A0, 0), Nc - 1)];
+            const bool ok = (r < A0) ? r < A : (r < T && n >= 0);
+            const uint64_t m = __ballot(ok);
+            if (lane == 0) {
+                cflag_s[base / kChunk] = static_cast<int32_t>(static_cast<uint32_t>(m));
+                if (base / kChunk + 1 < nchunks)
+                    cflag_s[base / kChunk + 1] = static_cast<int32_t>(static_cast<uint32_t>(m >> 32));
+            }
+        }
+        // (the barrier after the first chunk's tile stores orders these)
+    }
     put(0, 0, sk, sv);
     __syncthreads();
-    auto step = [&](int c, auto buf_tag, auto full_tag, auto first_tag) __attribute__((always_inline)) {
+    auto step = [&](int c, auto buf_tag, auto full_tag, auto first_tag, uint32_t rows = ~0u) __attribute__((always_inline)) {
         constexpr int BI = decltype(buf_tag)::value;
         load(min(c + 1, nchunks - 1), sk, sv);
-        if (nq > 0) compute(c, BI, full_tag, first_tag);
+        if (nq > 0) compute(c, BI, rows, full_tag, first_tag);
         put(BI ^ 1, c + 1, sk, sv);
         __syncthreads();
     };
-    // The chunks without rows past A, in pairs (constant buffer indices),
-    // then the partial last chunk if A is not a multiple of 32: only that
-    // one carries the masking.
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    using T = std::true_type;
-    using F = std::false_type;
-    const int nfull = A / kChunk;  // >= 2 (A > 64)
-    step(0, B0{}, T{}, T{});
-    int c = 1;
-    for (; c + 1 < nfull; c += 2) {
-        step(c, B1{}, T{}, F{});
-        step(c + 1, B0{}, T{}, F{});
-    }
-    if (c < nfull) step(c++, B1{}, T{}, F{});
-    if (c < nchunks) {
-        if (c & 1)
-            step(c, B1{}, F{}, F{});
-        else
-            step(c, B0{}, F{}, F{});
+    using T1 = std::true_type;
+    using F0 = std::false_type;
+    if constexpr (!CACHED) {
+        // The chunks without rows past A, in pairs (constant buffer indices),
+        // then the partial last chunk if A is not a multiple of 32: only that
+        // one carries the masking.
+        const int nfull = A / kChunk;  // >= 2 (A > 64)
+        step(0, B0{}, T1{}, T1{});
+        int c = 1;
+        for (; c + 1 < nfull; c += 2) {
+            step(c, B1{}, T1{}, F0{});
+            step(c + 1, B0{}, T1{}, F0{});
+        }
+        if (c < nfull) step(c++, B1{}, T1{}, F0{});
+        if (c < nchunks) {
+            if (c & 1)
+                step(c, B1{}, F0{}, F0{});
+            else
+                step(c, B0{}, F0{}, F0{});
+        }
+    } else {
+        // Chunk 0 holds active rows only (A > 64); later chunks take the
+        // masked path when their flag says a row is missing (uniform).
+        auto step_any = [&](int c, auto buf_tag) __attribute__((always_inline)) {
+            step(c, buf_tag, T1{}, F0{},
+                 __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cflag_s[c])));
+        };
+        step(0, B0{}, T1{}, T1{});
+        int c = 1;
+        for (; c + 1 < nchunks; c += 2) {
+            step_any(c, B1{});
+            step_any(c + 1, B0{});
+        }
+        if (c < nchunks) step_any(c, B1{});
     }
 
     // Finalise through this wave's 2 KB of the (now free) LDS tiles, one
@@ -1020,12 +1173,43 @@ int launch_dense_wg(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_
     constexpr int kPerBlock = kWgWaves * 16 * kWgNqt;
     const int nb = (A + kPerBlock - 1) / kPerBlock;
     const int grid = (nb == 1) ? units : ((units + 7) / 8) * 8 * nb;
-    hipLaunchKernelGGL((attn_dense_wg_kernel<kWgNqt, UPDATE>), dim3(grid), dim3(64 * kWgWaves), 0,
-                       stream, q_a, k_a, v_a, k_cache, v_cache, out, lse, units, A, nb,
-                       scale_log2);
+    // the list area is unused without cached rows: one entry and one flag
+    hipLaunchKernelGGL((attn_wg_kernel<kWgNqt, kWgWaves, UPDATE, false>), dim3(grid),
+                       dim3(64 * kWgWaves), 0, stream, q_a, k_a, v_a, k_cache, v_cache, out, lse,
+                       units, A, nb, scale_log2, nullptr, 0, H, A, 0, nullptr, 0, nullptr);
     return status_from_launch();
 }
 
+// Dynamic LDS of the cached workgroup kernel: the staged list, the chunk
+// flags and (UPDATE) the active positions.
+inline size_t cached_wg_lds(bool update, int A, int Nc) {
+    const int nchunks = (A + Nc + kChunk - 1) / kChunk;
+    return static_cast<size_t>((Nc > 0 ? Nc : 1) + nchunks + (update ? A : 0)) * 4;
+}
+constexpr size_t kCachedWgMaxLds = 48 * 1024;  // + 16 KB of tiles: 64 KB per workgroup
+
+template <bool UPDATE>
+int launch_cached_wg(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
+                     const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* cached_idx,
+                     int ldc, uint16_t* out, float* lse, int B, int H, int N, int A, int Nc,
+                     float scale_log2, const int32_t* active_idx, int ld_act, int32_t* err_count,
+                     hipStream_t stream) {
+    const int units = B * H;
+    const size_t lds = cached_wg_lds(UPDATE, A, Nc);  // <= kCachedWgMaxLds (checked by the caller)
+    auto go = [&](auto waves_tag) {
+        constexpr int kW = decltype(waves_tag)::value;
+        constexpr int kPerBlock = kW * 64;
+        const int nb = (A + kPerBlock - 1) / kPerBlock;
+        const int grid = (nb == 1) ? units : ((units + 7) / 8) * 8 * nb;
+        hipLaunchKernelGGL((attn_wg_kernel<4, kW, UPDATE, true>), dim3(grid), dim3(64 * kW), lds,
+                           stream, q_a, k_a, v_a, const_cast<uint16_t*>(k_cache),
+                           const_cast<uint16_t*>(v_cache), out, lse, units, A, nb, scale_log2,
+                           cached_idx, ldc, H, N, Nc, active_idx, ld_act, err_count);
+        return status_from_launch();
+    };
+    // two waves up to 128 queries, four beyond (more blocks past 256)
+    return (A <= 2 * 64) ? go(std::integral_constant<int, 2>{}) : go(std::integral_constant<int, 4>{});
+}
 template <int NQT, bool UPDATE>
 int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
                 const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* cached_idx,
@@ -1157,6 +1341,15 @@ int dispatch_mfma(const uint16_t* q, const uint16_t* ka, const uint16_t* va, con
                                        const_cast<uint16_t*>(vc), o, lse, B, H, A, scale_log2,
                                        stream);
     const int n_groups = (A + kQueriesPerGroup - 1) / kQueriesPerGroup;
+    // Cached rows and several query groups per unit: the workgroup kernel
+    // shares each chunk among the unit's groups, unless there are so few
+    // units that several waves per unit (one per chunk range) fill the chip
+    // better, or the staged lists would not fit.
+    if (a_len == nullptr && Nc > 0 && n_groups > 1 &&
+        cached_wg_lds(UPDATE, A, Nc) <= kCachedWgMaxLds &&
+        split_for(B * H, n_groups, (A + Nc + kChunk - 1) / kChunk, 4) == 1)
+        return launch_cached_wg<UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
+                                        Nc, scale_log2, active_idx, ld_act, err_count, stream);
     const int nqt = (n_groups > 1) ? 4 : (A + 15) / 16;
     switch (nqt) {
         case 1:

@@ -1,0 +1,120 @@
+"""GPU parity of the workgroup path of cache-aware attention: with more than 64
+active queries per (sequence, head) unit and many units, the library runs one
+workgroup per unit (per block of 128 or 256 of its queries) whose waves share
+each K/V chunk of the unit's [active ; cached] sequence through LDS.
+
+Each case draws two sequences x two heads and tiles them into a batch of 160
+sequences (320 units, enough for this path), runs the batch once, checks that
+every copy computed the same thing, and checks the first two sequences
+against the oracle (bf16 max-abs 2e-2, log-sum-exp 4.5e-3).  The cases cover a
+complete and a ragged last chunk, query counts that leave partial query tiles
+and idle waves, two and four waves per workgroup, two query blocks per unit,
+and skipped cached entries (-1 and past N), which send their chunks down the
+masked path.  The fused cache update must give the same output bits, write
+the active rows exactly once (only the unit's first block writes) and count
+each skipped active entry once per sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mar_workloads import device_normal
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+TILE = 80
+
+# (N, A, Nc, skipped cached entries per sequence)
+CASES = [(1088, 128, 960, 0),   # the high-res layer: 2 waves, 34 complete chunks
+         (400, 100, 270, 0),    # T = 370: a ragged last chunk; 36 queries in the second wave
+         (700, 65, 600, 9),     # skipped entries: masked chunks; a 1-query tile
+         (900, 200, 650, 0),    # 4 waves, the last with 8 queries
+         (1200, 300, 880, 5)]   # 2 blocks of 256 queries per unit
+
+
+@pytest.fixture(scope="module")
+def marca():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import cache_aware_attention_amd as m
+    return m
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def raw(t):
+    return t.detach().contiguous().cpu().view(torch.int16).numpy()
+
+
+def case(N, A, Nc, n_skip, seed):
+    B, H = 2, 2
+    q, ka, va = (device_normal((B, H, A, 64), seed + i, DEV, torch.bfloat16) for i in range(3))
+    kc, vc = (device_normal((B, H, N, 64), seed + 3 + i, DEV, torch.bfloat16) for i in range(2))
+    g = torch.Generator().manual_seed(seed)
+    perms = [torch.randperm(N, generator=g) for _ in range(B)]
+    active = torch.stack([p[:A] for p in perms]).to(torch.int32)
+    cached = torch.stack([p[A:A + Nc] for p in perms]).to(torch.int32)
+    if n_skip:
+        pos = torch.randperm(Nc, generator=g)[:n_skip]
+        cached[0, pos[::2]] = -1
+        cached[0, pos[1::2]] = N + 5
+    tile = lambda t: t.repeat(TILE, *([1] * (t.dim() - 1))).contiguous()
+    return [tile(t) for t in (q, ka, va, kc, vc)], tile(active).to(DEV), tile(cached).to(DEV)
+
+
+def check_oracle(ts, cached, Nc, out, lse):
+    """The library skips a cached entry outside [0, N); the oracle takes the
+    list without it."""
+    import oracle
+    q, ka, va, kc, vc = ts
+    N = kc.shape[2]
+    cl = cached.cpu().numpy()
+    for b in range(2):
+        keep = cl[b, :Nc][(cl[b, :Nc] >= 0) & (cl[b, :Nc] < N)][None, :]
+        for h in range(2):
+            sl = lambda t: f64(t[b:b + 1, h:h + 1])
+            o, l = oracle.cache_attention(sl(q), sl(ka), sl(va), sl(kc), sl(vc), keep, 0.125,
+                                          Nc=keep.shape[1])
+            assert np.abs(f64(out[b, h]) - o[0, 0]).max() <= 2e-2, (b, h)
+            assert np.abs(f64(lse[b, h]) - l[0, 0]).max() <= 4.5e-3, (b, h)
+
+
+@pytest.mark.parametrize("N,A,Nc,n_skip", CASES)
+def test_cached_workgroup_attention(marca, N, A, Nc, n_skip):
+    ts, active, cached = case(N, A, Nc, n_skip, seed=7 * N + A)
+    B = ts[0].shape[0]
+    lse = torch.empty((B, 2, A), dtype=torch.float32, device=DEV)
+    out = marca.mar_cache_attn_fwd(*ts, cached, Nc=Nc, lse=lse)
+    torch.cuda.synchronize()
+    for t in range(1, TILE):
+        assert torch.equal(out[2 * t:2 * t + 2], out[:2])
+    check_oracle(ts, cached, Nc, out, lse)
+
+
+@pytest.mark.parametrize("N,A,Nc,n_skip", [CASES[0], CASES[2], CASES[4]])
+def test_cached_workgroup_fused_update(marca, N, A, Nc, n_skip):
+    import oracle
+    ts, active, cached = case(N, A, Nc, n_skip, seed=11 * N + A)
+    q, ka, va, kc, vc = ts
+    B = q.shape[0]
+    # two skipped active entries in the first sequence (each copy of it)
+    active[0::2, 3] = -1
+    active[0::2, A - 1] = N
+    out = marca.mar_cache_attn_fwd(*ts, cached, Nc=Nc)
+    kc2, vc2 = kc.clone(), vc.clone()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out2 = marca.mar_cache_attn_fwd_update(q, ka, va, kc2, vc2, cached, active, Nc=Nc,
+                                           err_count=err)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+    # once per sequence (not per head): 2 per copy of the first sequence
+    assert int(err.item()) == 2 * TILE
+    kr, vr, skipped = oracle.kv_scatter(raw(kc[:2]), raw(vc[:2]), raw(ka[:2]), raw(va[:2]),
+                                        active[:2].cpu().numpy())
+    assert skipped == 2
+    assert np.array_equal(raw(kc2[:2]), kr) and np.array_equal(raw(vc2[:2]), vr)
+    for t in range(1, TILE):
+        assert torch.equal(kc2[2 * t:2 * t + 2], kc2[:2]) and torch.equal(vc2[2 * t:2 * t + 2], vc2[:2])
