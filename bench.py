@@ -188,6 +188,73 @@ def seq_view(x, nb):
     return v
 
 
+def other_configs(marca, dev, stream):
+    """The cache-aware attention call (and, at the high-res length, the full
+    attention and refresh-step calls) at the other configurations' shapes:
+    time per call over rotating layers whose working set is well above the
+    256 MB last-level cache, HIP events around R passes after a warm-up."""
+    import torch
+
+    from mar_workloads import CONFIGS, attention_inputs
+    res = {}
+    for name, n_layers in (("mar_b", 12), ("mar_h", 4), ("highres", 4)):
+        cfg = CONFIGS[name]
+        layers = []
+        for l in range(n_layers):
+            x = attention_inputs(cfg, dev, seed=cfg.seed * 100 + 50 + l)
+            x["out"] = torch.empty_like(x["q_a"])
+            layers.append(x)
+        torch.cuda.synchronize()
+
+        def timed(fn, R=5):
+            # warm up for at least 50 ms: right after the inputs are built the
+            # first passes run measurably slower
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.05:
+                for L in layers:
+                    fn(L)
+                torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(R):
+                for L in layers:
+                    fn(L)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (R * len(layers))
+
+        us = timed(lambda L: marca.mar_cache_attn_fwd(L["q_a"], L["k_a"], L["v_a"], L["k_cache"],
+                                                      L["v_cache"], L["cached"], Nc=cfg.Nc,
+                                                      out=L["out"]))
+        nbytes = attn_bytes(cfg.B, cfg.H, cfg.A, cfg.Nc, cfg.D)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        entry = {"sequences": cfg.B, "heads": cfg.H, "tokens": cfg.N, "active": cfg.A,
+                 "cached": cfg.Nc, "attn_us_per_call": us, "attn_gbs": gbs,
+                 "attn_frac_hbm": gbs / PEAK_HBM_GBS, "attn_bytes_per_call": nbytes,
+                 "attn_tflops": 4 * cfg.B * cfg.H * cfg.A * (cfg.A + cfg.Nc) * cfg.D / us / 1e6}
+        if name == "highres":
+            full = torch.empty_like(layers[0]["k_cache"])
+            flops = 4 * cfg.B * cfg.H * cfg.N * cfg.N * cfg.D
+            f_us = timed(lambda L: marca.mar_cache_attn_fwd(L["k_cache"], L["k_cache"], L["v_cache"],
+                                                            L["k_cache"], L["v_cache"], None, Nc=0,
+                                                            out=full))
+            entry["full_attn_us_per_call"] = f_us
+            entry["full_attn_tflops"] = flops / f_us / 1e6
+            # refresh step: each layer's caches take the next layer's rows as
+            # fresh K/V; the queries come from the layer after that
+            nxt = {id(L): (layers[(i + 1) % len(layers)], layers[(i + 2) % len(layers)])
+                   for i, L in enumerate(layers)}
+            entry["refresh_us_per_call"] = timed(
+                lambda L: marca.mar_cache_attn_fwd_update(
+                    nxt[id(L)][1]["k_cache"], nxt[id(L)][0]["k_cache"], nxt[id(L)][0]["v_cache"],
+                    L["k_cache"], L["v_cache"], None, None, Nc=0, out=full))
+        res[name] = entry
+        del layers
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -482,6 +549,8 @@ def main():
     except Exception as exc:  # noqa: BLE001 - reported, not fatal
         print(f"bench: copy measurement failed: {exc}", file=sys.stderr)
 
+    configs = None if args.no_decode else other_configs(marca, dev, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: oracle CPU baseline", file=sys.stderr, flush=True)
@@ -531,6 +600,7 @@ def main():
             "speedup": decode_ms.get("none", 0) / decode_ms.get("cache", 1),
             "ms_cond_cache": decode_ms.get("cache+cond"),
             "speedup_cond_cache": decode_ms.get("none", 0) / decode_ms.get("cache+cond", 1)},
+        "configs": configs,
         "attn_bytes_per_call": bytes_call,
         "attn_tok_per_s": cfg.B * cfg.A / (avg_us["attn"] * 1e-6),
         "copy_gbs": copy_gbs,
