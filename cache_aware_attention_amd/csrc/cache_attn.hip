@@ -1002,9 +1002,12 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
         };
         // Query tiles in pairs: both tiles' chains sit in one basic block
         // (one rescale test per pair), so their instructions interleave.
+        // Every tile is computed, also past nq (those rows repeat the last
+        // query and are never stored): a per-pair test would end the basic
+        // block before the next pair's score MFMAs, which then could not
+        // issue among this pair's exponentials.
 #pragma unroll
         for (int qt = 0; qt < NQT; qt += 2) {
-            if (qt * 16 >= nq) continue;  // wave-uniform
             if (qt + 1 < NQT) {
                 float x0[8], x1[8];
                 scores(qt, x0);
