@@ -493,7 +493,22 @@ def main():
     torch.cuda.synchronize()
     ms_per_step_fused = f0.elapsed_time(f1) / args.steps
 
-    # Timed region 1c: whole decodes, with and without the cache.
+    # Timed region 2: the same launches, grouped per kernel, HIP events per group.
+    # Timed before the decodes, whose second of heavy load slows later groups.
+    # One untimed pass first: the first span of the first pass would otherwise
+    # take in the host's delay before its first launch.
+    # At most 30 passes (900 launches of each kernel): over longer runs of
+    # these back-to-back heavy groups the later ones slow down (the refresh
+    # layers by 10-15%), which is the chip's sustained-load behaviour, not
+    # the kernels'.
+    timed_kernels()
+    torch.cuda.synchronize()
+    groups = [timed_kernels() for _ in range(min(args.steps, 30))]
+    torch.cuda.synchronize()
+    avg_us = {k: 1e3 * sum(g[k][0].elapsed_time(g[k][1]) for g in groups)
+              / sum(g[k][2] for g in groups) for k in groups[0]}
+
+    # Timed region 3: whole decodes, with and without the caches.
     decode_ms = {}
     for mode in (() if args.no_decode else ("cache", "none", "cache+cond")):
         run = lambda: decode(mode != "none", cond_cache=mode == "cache+cond")
@@ -508,19 +523,6 @@ def main():
     n_refresh_steps = sum(marca.mar_plan_step(decode_counts, t, cfg.N, cfg.budget).refresh
                           for t in range(cfg.steps))
 
-    # Timed region 2: the same launches, grouped per kernel, HIP events per group.
-    # One untimed pass first: the first span of the first pass would otherwise
-    # take in the host's delay before its first launch after the decodes.
-    # At most 30 passes (900 launches of each kernel): over longer runs of
-    # these back-to-back heavy groups the later ones slow down (the refresh
-    # layers by 10-15%), which is the chip's sustained-load behaviour, not
-    # the kernels'.
-    timed_kernels()
-    torch.cuda.synchronize()
-    groups = [timed_kernels() for _ in range(min(args.steps, 30))]
-    torch.cuda.synchronize()
-    avg_us = {k: 1e3 * sum(g[k][0].elapsed_time(g[k][1]) for g in groups)
-              / sum(g[k][2] for g in groups) for k in groups[0]}
 
     tokens_per_step = cfg.B * cfg.A * n_ca
     value = tokens_per_step / (ms_per_step * 1e-3)
