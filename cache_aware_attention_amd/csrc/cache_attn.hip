@@ -1186,7 +1186,9 @@ int launch_dense_wg(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_
 // Dynamic LDS of the cached workgroup kernel: the staged list, the chunk
 // flags and (UPDATE) the active positions.
 inline size_t cached_wg_lds(bool update, int A, int Nc) {
-    const int nchunks = (A + Nc + kChunk - 1) / kChunk;
+    // the kernel's chunk count: the active rows padded to whole chunks, then
+    // the cached rows
+    const int nchunks = (A + kChunk - 1) / kChunk + (Nc + kChunk - 1) / kChunk;
     return static_cast<size_t>((Nc > 0 ? Nc : 1) + nchunks + (update ? A : 0)) * 4;
 }
 constexpr size_t kCachedWgMaxLds = 48 * 1024;  // + 16 KB of tiles: 64 KB per workgroup

@@ -30,7 +30,12 @@ CASES = [(1088, 128, 960, 0),   # the high-res layer: 2 waves, 34 complete chunk
          (400, 100, 270, 0),    # T = 370: a ragged last chunk; 36 queries in the second wave
          (700, 65, 600, 9),     # skipped entries: masked chunks; a 1-query tile
          (900, 200, 650, 0),    # 4 waves, the last with 8 queries
-         (1200, 300, 880, 5)]   # 2 blocks of 256 queries per unit
+         (1200, 300, 880, 5),   # 2 blocks of 256 queries per unit
+         # The active rows fill ceil(A/32) chunks and the cached rows start on the
+         # next one, so the staged lists need ceil(A/32) + ceil(Nc/32) chunk masks.
+         # Here the staged lists take exactly 128 entries (512 bytes, no rounding
+         # slack) and that count is one more than ceil((A + Nc)/32).
+         (300, 100, 121, 0)]
 
 
 @pytest.fixture(scope="module")
@@ -94,7 +99,8 @@ def test_cached_workgroup_attention(marca, N, A, Nc, n_skip):
     check_oracle(ts, cached, Nc, out, lse)
 
 
-@pytest.mark.parametrize("N,A,Nc,n_skip", [CASES[0], CASES[2], CASES[4]])
+@pytest.mark.parametrize("N,A,Nc,n_skip", [CASES[0], CASES[2], CASES[4],
+                                            (200, 100, 24, 0)])  # lists + masks: 128 entries
 def test_cached_workgroup_fused_update(marca, N, A, Nc, n_skip):
     import oracle
     ts, active, cached = case(N, A, Nc, n_skip, seed=11 * N + A)
