@@ -724,10 +724,13 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 //    says whether every row of the chunk exists; only chunks without that
 //    flag carry the masking.  With UPDATE the loading lanes of the unit's
 //    first block write the active rows into the caches at active_idx.
+//    RAGGED: per-sequence counts, min(a_len[b], A) active rows and
+//    min(c_len[b], Nc) cached entries (A and Nc stay the row stride and the
+//    list capacity); rows past a sequence's active count are not written.
 // The MFMA tiles are those of attn_mfma_kernel.  The softmax state differs:
 //  * each query keeps one reference mc, a maximum of its scaled scores
-//    s * scale_log2, set from the first chunk (A > 64 active rows, so the
-//    first chunk is always complete);
+//    s * scale_log2, set from the first chunk (active rows, at least the
+//    first of which exists, so the reference is finite);
 //  * a tile computes x = s * scale_log2 - mc first and tests max(x) against
 //    kRescaleLog2 (an inline constant), so no raw maximum or threshold has
 //    to stay in registers;
@@ -740,15 +743,18 @@ constexpr int kWgWaves = 4;
 constexpr int kWgNqt = 5;
 constexpr int kWgTile = kChunk * 128;  // bytes of one K or V chunk tile
 
-template <int NQT, int W, bool UPDATE, bool CACHED>
+template <int NQT, int W, bool UPDATE, bool CACHED, bool RAGGED = false>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
                     const uint16_t* __restrict__ v_a, uint16_t* k_cache, uint16_t* v_cache,
                     uint16_t* __restrict__ out, float* __restrict__ lse, int units, int A,
                     int n_blocks, float scale_log2, const int32_t* __restrict__ cached_idx,
                     int ldc, int H, int N, int Nc, const int32_t* __restrict__ active_idx,
-                    int ld_act, int32_t* __restrict__ err_count) {
+                    int ld_act, int32_t* __restrict__ err_count,
+                    const int32_t* __restrict__ a_len = nullptr,
+                    const int32_t* __restrict__ c_len = nullptr) {
     static_assert(W == 1 || W == 2 || W == 4, "waves per workgroup");
+    static_assert(!RAGGED || (CACHED && !UPDATE), "per-sequence counts: cached rows, no update");
     constexpr int kQ = 16 * NQT;         // queries per wave
     constexpr int kPasses = 4 / W;       // load passes per chunk (8 W rows each)
     __shared__ __align__(16) unsigned char lds[4 * kWgTile];  // 2 buffers x (K tile, V tile)
@@ -773,14 +779,22 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
         qb = slot % n_blocks;
         if (u >= units) return;  // uniform over the workgroup, before any barrier
     }
+    // The unit's counts: An active rows (A is their stride) and Ncn cached
+    // entries (Nc is the list capacity).
+    int An = A, Ncn = Nc;
+    if constexpr (RAGGED) {
+        An = min(max(a_len[u / H], 0), A);
+        Ncn = min(max(c_len[u / H], 0), Nc);
+        if (qb * W * kQ >= An) return;  // no queries in this block (uniform, before any barrier)
+    }
     const int q0 = (qb * W + w) * kQ;
-    const int nq = min(A - q0, kQ);  // <= 0: the wave loads and waits, computes nothing
+    const int nq = min(An - q0, kQ);  // <= 0: the wave loads and waits, computes nothing
     const size_t ub = static_cast<size_t>(u) * A * kD;
     // CACHED: the active rows fill chunks [0, na) (the last one padded), the
     // cached rows start on the next chunk: row A0 + j is cached entry j.
-    const int na = (A + kChunk - 1) / kChunk;
+    const int na = (An + kChunk - 1) / kChunk;
     const int A0 = CACHED ? na * kChunk : A;
-    const int T = CACHED ? A0 + Nc : A;  // rows of the unit's (padded) sequence
+    const int T = CACHED ? A0 + Ncn : A;  // rows of the unit's (padded) sequence
     const int nchunks = (T + kChunk - 1) / kChunk;
     const __amdgpu_buffer_rsrc_t rka = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(k_a + ub), 0, A * kD * 2, 0x00020000);
@@ -807,7 +821,7 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
         };
         const int r0 = c * kChunk;
         const uint32_t piece = 16 * (tid & 7);
-        if (!CACHED || r0 < A) {  // active rows (uniform; a row past A reads as zero)
+        if (!CACHED || r0 < An) {  // active rows (uniform; a row past A reads as zero)
 #pragma unroll
             for (int p = 0; p < kPasses; ++p) {
                 const uint32_t ofs = static_cast<uint32_t>(r0 + 8 * W * p + lrow) * (kD * 2) + piece;
@@ -819,7 +833,7 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
             for (int p = 0; p < kPasses; ++p) {
                 const int j = r0 - A0 + 8 * W * p + lrow;
                 const int n = cidx_s[min(j, Nc - 1)];
-                const uint32_t ofs = (j < Nc && n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) + piece : kOut;
+                const uint32_t ofs = (j < Ncn && n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) + piece : kOut;
                 kk[p] = ld(rkc, ofs);
                 vv[p] = ld(rvc, ofs);
             }
@@ -863,7 +877,7 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     bf16x8_t qf[NQT][2];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-        const int qi = max(min(q0 + qt * 16 + m16, A - 1), 0);
+        const int qi = max(min(q0 + qt * 16 + m16, An - 1), 0);
         const uint4* p = reinterpret_cast<const uint4*>(q_a + ub + static_cast<size_t>(qi) * kD);
         qf[qt][0] = as_bf16x8(p[g]);
         qf[qt][1] = as_bf16x8(p[4 + g]);
@@ -884,7 +898,7 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     }
 
     // mc: the reference maximum of each query's scaled scores s * scale_log2
-    // (set from the first chunk, which is complete since A > 64).
+    // (set from the first chunk: active rows, the first of which exists).
     float mc[NQT];
     f32x4_t oacc[NQT][4], lacc[NQT];
 #pragma unroll
@@ -1051,14 +1065,14 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
 #pragma unroll
         for (int k = 0; k < kStage; ++k) {
             const int c = tid + 64 * W * k;
-            iv[k] = (c < Nc) ? cg[c] : -1;
+            iv[k] = (c < Ncn) ? cg[c] : -1;
         }
 #pragma unroll
         for (int k = 0; k < kStage; ++k) {
             const int c = tid + 64 * W * k;
-            if (c < Nc) cidx_s[c] = (iv[k] >= 0 && iv[k] < N) ? iv[k] : -1;
+            if (c < Ncn) cidx_s[c] = (iv[k] >= 0 && iv[k] < N) ? iv[k] : -1;
         }
-        for (int c = tid + 64 * W * kStage; c < Nc; c += 64 * W) {
+        for (int c = tid + 64 * W * kStage; c < Ncn; c += 64 * W) {
             const int n = cg[c];
             cidx_s[c] = (n >= 0 && n < N) ? n : -1;
         }
@@ -1079,7 +1093,7 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
         for (int base = 64 * w; base < nchunks * kChunk; base += 64 * W) {
             const int r = base + lane;
             const int n = cidx_s[min(max(r - A0, 0), Nc - 1)];
-            const bool ok = (r < A0) ? r < A : (r < T && n >= 0);
+            const bool ok = (r < A0) ? r < An : (r < T && n >= 0);
             const uint64_t m = __ballot(ok);
             if (lane == 0) {
                 cflag_s[base / kChunk] = static_cast<int32_t>(static_cast<uint32_t>(m));
@@ -1121,13 +1135,14 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
                 step(c, B0{}, F0{}, F0{});
         }
     } else {
-        // Chunk 0 holds active rows only (A > 64); later chunks take the
-        // masked path when their flag says a row is missing (uniform).
+        // Every chunk's scores start from its row mask (uniform).  Chunk 0
+        // sets the references; it holds active rows only, all of them unless
+        // a sequence's count is below 32.
         auto step_any = [&](int c, auto buf_tag) __attribute__((always_inline)) {
             step(c, buf_tag, T1{}, F0{},
                  __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cflag_s[c])));
         };
-        step(0, B0{}, T1{}, T1{});
+        step(0, B0{}, T1{}, T1{}, __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cflag_s[0])));
         int c = 1;
         for (; c + 1 < nchunks; c += 2) {
             step_any(c, B1{});
@@ -1193,12 +1208,12 @@ inline size_t cached_wg_lds(bool update, int A, int Nc) {
 }
 constexpr size_t kCachedWgMaxLds = 48 * 1024;  // + 16 KB of tiles: 64 KB per workgroup
 
-template <bool UPDATE>
+template <bool UPDATE, bool RAGGED>
 int launch_cached_wg(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
                      const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* cached_idx,
                      int ldc, uint16_t* out, float* lse, int B, int H, int N, int A, int Nc,
                      float scale_log2, const int32_t* active_idx, int ld_act, int32_t* err_count,
-                     hipStream_t stream) {
+                     const int32_t* a_len, const int32_t* c_len, hipStream_t stream) {
     const int units = B * H;
     const size_t lds = cached_wg_lds(UPDATE, A, Nc);  // <= kCachedWgMaxLds (checked by the caller)
     auto go = [&](auto waves_tag) {
@@ -1206,10 +1221,11 @@ int launch_cached_wg(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v
         constexpr int kPerBlock = kW * 64;
         const int nb = (A + kPerBlock - 1) / kPerBlock;
         const int grid = (nb == 1) ? units : ((units + 7) / 8) * 8 * nb;
-        hipLaunchKernelGGL((attn_wg_kernel<4, kW, UPDATE, true>), dim3(grid), dim3(64 * kW), lds,
-                           stream, q_a, k_a, v_a, const_cast<uint16_t*>(k_cache),
+        hipLaunchKernelGGL((attn_wg_kernel<4, kW, UPDATE, true, RAGGED>), dim3(grid), dim3(64 * kW),
+                           lds, stream, q_a, k_a, v_a, const_cast<uint16_t*>(k_cache),
                            const_cast<uint16_t*>(v_cache), out, lse, units, A, nb, scale_log2,
-                           cached_idx, ldc, H, N, Nc, active_idx, ld_act, err_count);
+                           cached_idx, ldc, H, N, Nc, active_idx, ld_act, err_count, a_len,
+                           c_len);
         return status_from_launch();
     };
     // two waves up to 128 queries, four beyond (more blocks past 256)
@@ -1346,15 +1362,22 @@ int dispatch_mfma(const uint16_t* q, const uint16_t* ka, const uint16_t* va, con
                                        const_cast<uint16_t*>(vc), o, lse, B, H, A, scale_log2,
                                        stream);
     const int n_groups = (A + kQueriesPerGroup - 1) / kQueriesPerGroup;
-    // Cached rows and several query groups per unit: the workgroup kernel
-    // shares each chunk among the unit's groups, unless there are so few
-    // units that several waves per unit (one per chunk range) fill the chip
-    // better, or the staged lists would not fit.
-    if (a_len == nullptr && Nc > 0 && n_groups > 1 &&
-        cached_wg_lds(UPDATE, A, Nc) <= kCachedWgMaxLds &&
-        split_for(B * H, n_groups, (A + Nc + kChunk - 1) / kChunk, 4) == 1)
-        return launch_cached_wg<UPDATE>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A,
-                                        Nc, scale_log2, active_idx, ld_act, err_count, stream);
+    // Cached rows and several query groups per unit (capacities, with
+    // per-sequence counts): the workgroup kernel shares each chunk among the
+    // unit's groups, unless there are so few units that several waves per
+    // unit (one per chunk range) fill the chip better, or the staged lists
+    // would not fit.
+    if (Nc > 0 && n_groups > 1 && cached_wg_lds(UPDATE, A, Nc) <= kCachedWgMaxLds &&
+        split_for(B * H, n_groups, (A + Nc + kChunk - 1) / kChunk, 4) == 1) {
+        if (a_len == nullptr)
+            return launch_cached_wg<UPDATE, false>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B,
+                                                   H, N, A, Nc, scale_log2, active_idx, ld_act,
+                                                   err_count, nullptr, nullptr, stream);
+        if constexpr (!UPDATE)
+            return launch_cached_wg<false, true>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H,
+                                                 N, A, Nc, scale_log2, active_idx, ld_act,
+                                                 err_count, a_len, c_len, stream);
+    }
     const int nqt = (n_groups > 1) ? 4 : (A + 15) / 16;
     switch (nqt) {
         case 1:

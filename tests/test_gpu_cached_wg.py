@@ -124,3 +124,38 @@ def test_cached_workgroup_fused_update(marca, N, A, Nc, n_skip):
     assert np.array_equal(raw(kc2[:2]), kr) and np.array_equal(raw(vc2[:2]), vr)
     for t in range(1, TILE):
         assert torch.equal(kc2[2 * t:2 * t + 2], kc2[:2]) and torch.equal(vc2[2 * t:2 * t + 2], vc2[:2])
+
+
+@pytest.mark.parametrize("N,A,Nc,n_skip", [CASES[0], (700, 200, 480, 9), CASES[4]])
+def test_cached_workgroup_ragged(marca, N, A, Nc, n_skip):
+    """Per-sequence counts (LazyMAR's token cache): A and Nc are capacities;
+    rows past a sequence's active count stay untouched, a sequence with no
+    active rows writes nothing, and a block whose queries all lie past the
+    count returns at once."""
+    import oracle
+    ts, active, cached = case(N, A, Nc, n_skip, seed=13 * N + A)
+    B = ts[0].shape[0]
+    for an, cn in [(A, Nc), (0, Nc), (1, 0), (20, 7), (A // 2 + 3, Nc - 33), (A - 1, Nc)]:
+        a_len = torch.tensor([an, A - 5], dtype=torch.int32, device=DEV).repeat(TILE)
+        c_len = torch.tensor([cn, Nc // 2], dtype=torch.int32, device=DEV).repeat(TILE)
+        out = torch.full((B, 2, A, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((B, 2, A), 7.0, dtype=torch.float32, device=DEV)
+        marca.mar_cache_attn_fwd_ragged(*ts, cached, a_len, c_len, out=out, lse=lse)
+        torch.cuda.synchronize()
+        for t in range(1, TILE):
+            assert torch.equal(out[2 * t:2 * t + 2], out[:2]), (an, cn)
+        assert (out[0, :, an:].float() == 3.0).all() and (lse[0, :, an:] == 7.0).all()
+        assert (out[1, :, A - 5:].float() == 3.0).all()
+        q, ka, va, kc, vc = ts
+        cl = cached.cpu().numpy()
+        for b, (a_b, c_b) in enumerate([(an, cn), (A - 5, Nc // 2)]):
+            if a_b == 0:
+                continue
+            keep = cl[b, :c_b][(cl[b, :c_b] >= 0) & (cl[b, :c_b] < N)][None, :]
+            for h in range(2):
+                sl = lambda t, n=None: f64(t[b:b + 1, h:h + 1, :n])
+                o, l = oracle.cache_attention(sl(q, a_b), sl(ka, a_b), sl(va, a_b), sl(kc), sl(vc),
+                                              keep if keep.size else np.zeros((1, 1), np.int32),
+                                              0.125, Nc=keep.shape[1])
+                assert np.abs(f64(out[b, h, :a_b]) - o[0, 0]).max() <= 2e-2, (an, cn, b, h)
+                assert np.abs(f64(lse[b, h, :a_b]) - l[0, 0]).max() <= 4.5e-3, (an, cn, b, h)
