@@ -10,7 +10,7 @@
 // at each chunk boundary (the active/cached boundary among them) the state is
 // rescaled by 2^(m_old - m_new), which is the same merge rule.
 //
-// Two code paths:
+// Three code paths:
 //  * attn_mfma_kernel (bf16, A >= 16): one wave per (sequence, head) unit and
 //    query group of up to 64 queries.  S^T = K Q^T and O^T = V^T P^T run on
 //    v_mfma_f32_16x16x32_bf16; K goes straight from HBM into MFMA operand
@@ -20,12 +20,14 @@
 //    before the current chunk is computed.  The unit's cached index list is
 //    staged in LDS once.  Separate instantiations serve per-sequence counts,
 //    the fused cache update, and the case with no cached rows, whose keys are
-//    contiguous rows read at fixed per-lane offsets.
+//    contiguous rows read at fixed per-lane offsets.  With few units, several
+//    waves per unit each stream a range of its chunks and merge their states.
 //  * attn_wg_kernel (bf16, A > 64): a workgroup per unit (per block of its
 //    queries) shares each K/V chunk through a double-buffered LDS tile among
 //    its waves -- 4 waves x 80 queries without cached rows (the full-attention
-//    layers), 2 or 4 waves x 64 queries with them; the same MFMA tiles, with
-//    the softmax reference kept in scaled units and the query tiles in pairs.
+//    layers), 2 or 4 waves x 64 queries with them (also with per-sequence
+//    counts); the same MFMA tiles, with the softmax reference kept in scaled
+//    units and the query tiles in pairs.
 //  * attn_rowwise_kernel (fp32 any A, bf16 A < 16): one wave per query, one
 //    lane per head-dim element; plain FMA.  Exact-precision path for fp32.
 //
