@@ -1,0 +1,55 @@
+"""Host-side checks of bench.py (no GPU): the single-GPU guard, the algorithmic
+byte count of the attention roofline, and the rule that the counter-measured
+traffic is reported only for the kernel source it was taken on."""
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def load_bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_attention_algorithmic_bytes():
+    b = load_bench()
+    # MAR-L layer: 128 sequences x 16 heads, A = 48 active, Nc = 272 cached, D = 64, bf16.
+    # Q_A, K_A, V_A read and out written (4 x 48 rows), 272 cached K and V rows read,
+    # the 272-entry int32 list read once per sequence.
+    per_unit = (4 * 48 + 2 * 272) * 64 * 2
+    assert b.attn_bytes(128, 16, 48, 272, 64) == 128 * 16 * per_unit + 128 * 272 * 4
+    assert b.attn_bytes(128, 16, 48, 272, 64) == 193077248
+    # fp32 doubles the row bytes, not the list
+    assert b.attn_bytes(1, 1, 8, 56, 64, elem=4) == (4 * 8 + 2 * 56) * 64 * 4 + 56 * 4
+
+
+def test_traffic_only_for_the_measured_source(tmp_path):
+    b = load_bench()
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel v1\n")
+    rec = tmp_path / "traffic.json"
+    rec.write_text(json.dumps({"kernel_source_sha256_16": b.source_hash(str(src)),
+                               "hbm_bytes_per_launch": 123.0}))
+    b.TRAFFIC_FILE, b.ATTN_SRC = str(rec), str(src)
+    assert b.load_traffic(1) == 123.0
+    src.write_text("// kernel v2\n")  # the source changed since the counters were taken
+    assert b.load_traffic(1) is None
+    rec.write_text("not json")
+    assert b.load_traffic(1) is None
+    os.remove(rec)
+    assert b.load_traffic(1) is None
+
