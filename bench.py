@@ -67,6 +67,17 @@ def load_traffic(calls_bytes):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(x, plan_nc, cfg, args, budget_s=12.0):
     """The oracle on a bounded sample of the step: the top-K, the CFG residual and
     the gate once, then whole layer-calls of the attention (all 2048 (b,h) units)
@@ -119,6 +130,7 @@ def cpu_baseline(x, plan_nc, cfg, args, budget_s=12.0):
     tokens = cfg.B * cfg.A * n_ca
     return {
         "value": tokens / t_step, "unit": "tok/s", "cores": nt, "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"{n_layers} MAR-L layer-calls of attention (2048 (b,h) units each) and of "
                    f"the scatter, plus top-K, CFG residual and gate once; step time = fixed + "
                    f"{n_ca} x mean per-layer ({spent + t_attn + t_scatter:.1f} s of CPU work)"),
@@ -245,6 +257,14 @@ def other_configs(marca, dev, stream):
             # fresh K/V; the queries come from the layer after that
             nxt = {id(L): (layers[(i + 1) % len(layers)], layers[(i + 2) % len(layers)])
                    for i, L in enumerate(layers)}
+            # the token gate at this shape (W = 1024, C5's gated layers)
+            from mar_workloads import device_gate_features
+            gx, gy, _ = device_gate_features(cfg.B, cfg.N, 1024, seed=cfg.seed, device=dev)
+            g_us = timed(lambda L: marca.mar_cos_gate(gx, gy, 0.95))
+            g_bytes = 2 * cfg.B * cfg.N * 1024 * 2 + cfg.B * cfg.N * 9
+            entry["gate_us_per_call"] = g_us
+            entry["gate_gbs"] = g_bytes / (g_us * 1e-6) / 1e9
+            del gx, gy
             entry["refresh_us_per_call"] = timed(
                 lambda L: marca.mar_cache_attn_fwd_update(
                     nxt[id(L)][1]["k_cache"], nxt[id(L)][0]["k_cache"], nxt[id(L)][0]["v_cache"],
@@ -507,6 +527,8 @@ def main():
     torch.cuda.synchronize()
     avg_us = {k: 1e3 * sum(g[k][0].elapsed_time(g[k][1]) for g in groups)
               / sum(g[k][2] for g in groups) for k in groups[0]}
+    per_pass = sorted(1e3 * g["attn"][0].elapsed_time(g["attn"][1]) / g["attn"][2] for g in groups)
+    attn_median_us = per_pass[len(per_pass) // 2]
 
     # Timed region 3: whole decodes, with and without the caches.
     decode_ms = {}
@@ -603,6 +625,8 @@ def main():
             "ms_cond_cache": decode_ms.get("cache+cond"),
             "speedup_cond_cache": decode_ms.get("none", 0) / decode_ms.get("cache+cond", 1)},
         "configs": configs,
+        "attn_median_us": attn_median_us,
+        "attn_frac_of_copy": (achieved / copy_gbs) if copy_gbs else None,
         "attn_bytes_per_call": bytes_call,
         "attn_tok_per_s": cfg.B * cfg.A / (avg_us["attn"] * 1e-6),
         "copy_gbs": copy_gbs,
