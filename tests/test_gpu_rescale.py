@@ -11,7 +11,8 @@ the sequence and every kernel takes its rescale path repeatedly:
   without the refresh-step cache rewrite;
 * the one-wave cache-aware kernel (48 active queries, 272 cached rows), at
   many units (one wave per unit) and at few units (several waves per unit,
-  merged at the end), and fused with the cache update.
+  merged at the end), and the workgroup kernel with cached rows (128 active
+  queries), each also fused with the cache update.
 
 Every listed unit is checked against the oracle: bf16 max-abs 2e-2 on the
 outputs, 4.5e-3 on the log-sum-exp (the same bounds as elsewhere: the
@@ -76,9 +77,12 @@ def test_full_attention_rising_scores(marca, B, H, N):
     check(q, k, v, k, v, None, 0, out, lse, [(0, 0), (B - 1, H - 1), (B // 2, 1)])
 
 
-@pytest.mark.parametrize("B,H", [(40, 8), (2, 2)])  # one wave per unit / several waves per unit
-def test_cache_aware_rising_scores(marca, B, H):
-    N, A, Nc = 320, 48, 272
+@pytest.mark.parametrize("B,H,A", [(40, 8, 48),    # one wave per unit
+                                   (2, 2, 48),     # several waves per unit (few units)
+                                   (40, 8, 128)])  # a workgroup per unit (two query groups)
+def test_cache_aware_rising_scores(marca, B, H, A):
+    N = 320
+    Nc = N - A
     q, ka, va = (device_normal((B, H, A, 64), 950 + i, DEV, torch.bfloat16) for i in range(3))
     kc, vc = (device_normal((B, H, N, 64), 960 + i, DEV, torch.bfloat16) for i in range(2))
     q = (q.float() * 2.0).to(torch.bfloat16)
