@@ -6,8 +6,9 @@
 // computes one cosine per token (16-byte loads, float accumulation of <x,y>,
 // |x|^2, |y|^2 per lane, then a wave reduction) and the reuse decision
 // cos >= tau in float: several tokens per wave with all their loads in
-// flight for widths up to 256 pieces of 16 bytes, one token per wave above.  Kernel 2 (one workgroup per sequence) packs
-// the positions to recompute in ascending order with a block prefix sum.
+// flight for widths up to 256 pieces of 16 bytes, one token per wave above.
+// Kernel 2 (one workgroup per sequence) packs the positions to recompute in
+// ascending order with a block prefix sum.
 #include "device_util.h"
 #include "launch.h"
 
