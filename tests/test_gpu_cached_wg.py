@@ -159,3 +159,48 @@ def test_cached_workgroup_ragged(marca, N, A, Nc, n_skip):
                                               0.125, Nc=keep.shape[1])
                 assert np.abs(f64(out[b, h, :a_b]) - o[0, 0]).max() <= 2e-2, (an, cn, b, h)
                 assert np.abs(f64(lse[b, h, :a_b]) - l[0, 0]).max() <= 4.5e-3, (an, cn, b, h)
+
+
+def _sweep_shapes(n, seed):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        A = int(g.integers(65, 300))
+        N = int(g.integers(A + 1, 1400))
+        Nc = int(g.integers(1, N - A + 1))
+        out.append((N, A, Nc, int(g.integers(0, 2)) * 3))
+    return out
+
+
+@pytest.mark.parametrize("N,A,Nc,n_skip", _sweep_shapes(12, 2024),
+                         ids=lambda v: str(v))
+def test_cached_workgroup_sweep(marca, N, A, Nc, n_skip):
+    """Seeded random shapes through the workgroup path, with uniform and with
+    per-sequence counts, the first two sequences against the oracle."""
+    import oracle
+    ts, active, cached = case(N, A, Nc, n_skip, seed=3 * N + A + Nc)
+    B = ts[0].shape[0]
+    lse = torch.empty((B, 2, A), dtype=torch.float32, device=DEV)
+    out = marca.mar_cache_attn_fwd(*ts, cached, Nc=Nc, lse=lse)
+    torch.cuda.synchronize()
+    check_oracle(ts, cached, Nc, out, lse)
+
+    g = np.random.default_rng(N + A)
+    an = [int(g.integers(1, A + 1)), int(g.integers(1, A + 1))]
+    cn = [int(g.integers(0, Nc + 1)), int(g.integers(0, Nc + 1))]
+    a_len = torch.tensor(an, dtype=torch.int32, device=DEV).repeat(TILE)
+    c_len = torch.tensor(cn, dtype=torch.int32, device=DEV).repeat(TILE)
+    out = torch.full((B, 2, A, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    marca.mar_cache_attn_fwd_ragged(*ts, cached, a_len, c_len, out=out)
+    torch.cuda.synchronize()
+    q, ka, va, kc, vc = ts
+    cl = cached.cpu().numpy()
+    for b in range(2):
+        assert (out[b, :, an[b]:].float() == 3.0).all()
+        keep = cl[b, :cn[b]][(cl[b, :cn[b]] >= 0) & (cl[b, :cn[b]] < N)][None, :]
+        for h in range(2):
+            sl = lambda t, n=None: f64(t[b:b + 1, h:h + 1, :n])
+            o, _ = oracle.cache_attention(sl(q, an[b]), sl(ka, an[b]), sl(va, an[b]), sl(kc), sl(vc),
+                                          keep if keep.size else np.zeros((1, 1), np.int32),
+                                          0.125, Nc=keep.shape[1])
+            assert np.abs(f64(out[b, h, :an[b]]) - o[0, 0]).max() <= 2e-2, (b, h, an, cn)
