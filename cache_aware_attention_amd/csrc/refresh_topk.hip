@@ -10,11 +10,12 @@
 //
 // Kernel 1 (one workgroup per (sequence, head)) writes each token's
 // probability summed over the generating queries into a per-(b,h,token)
-// partial.  bf16: the score tiles run on MFMA; when the head's [queries x
-// keys] score block fits in LDS the keys are read once (scores kept in LDS,
-// then per-query max / sum, then per-key sums), otherwise two passes over
-// the keys (running (max, sum) per query, then normalised sums).  fp32 uses a
-// plain FMA version.
+// partial.  bf16: the score tiles run on MFMA.  Up to 16 generating queries
+// and 320 keys the scores stay in registers from the MFMA to the per-key
+// sums; otherwise, when the head's [queries x keys] score block fits in LDS,
+// the keys are read once (scores kept in LDS, then per-query max / sum, then
+// per-key sums), else two passes over the keys (running (max, sum) per
+// query, then normalised sums).  fp32 uses a plain FMA version.
 // Kernel 2 (one workgroup per sequence): sums the partials over heads in a
 // fixed order (no float atomics, deterministic), ranks the eligible tokens by
 // counting larger 64-bit keys with wave ballots (orderable score << 32 |
@@ -30,6 +31,9 @@ namespace {
 constexpr int kD = 64;
 constexpr int kThreads = 256;
 constexpr size_t kMaxScoreLds = 64 * 1024;  // single-pass scores when [QT*16][N+16] floats fit
+// Register-resident scores: 4 waves x 5 key tiles per unit (up to 320 keys).
+constexpr int kRegWaves = 4;
+constexpr int kRegTiles = 5;
 
 // Merge two running softmax states (max m, sum l) in base 2.
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
@@ -308,6 +312,127 @@ __global__ __launch_bounds__(kThreads) void refresh_scores_lds_kernel(
     }
 }
 
+// Register-resident bf16 path of kernel 1 for short sequences: up to 16
+// generating queries and at most W * TPW key tiles.  W waves per (sequence,
+// head) unit; wave w keeps the scores of its tiles t = w + W k (k < TPW) in
+// registers from the MFMA to the per-key sums, so nothing of the score block
+// goes through LDS (only the W partial row maxima and sums when W > 1).  At
+// 320 tokens and one wave per unit every unit of a decoding batch is resident
+// at once, two waves per SIMD, each with all of its key rows in flight.
+// The order of every reduction is fixed: over the wave's tiles in k order,
+// then a butterfly over the 16 lanes of a row, then over the waves in w
+// order, and per key over the four rows i of a lane, then across the lane
+// groups (xor 16, then xor 32); equal key rows therefore get equal scores.
+template <int TPW, int W>
+__global__ __launch_bounds__(64 * W) void refresh_scores_reg_kernel(
+    const uint16_t* __restrict__ q_gen, const uint16_t* __restrict__ k_full,
+    float* __restrict__ ws, int G, int N, float scale_log2) {
+    __shared__ float red[2][W][16];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = (W > 1) ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) : 0;
+    const int g = lane >> 4, m16 = lane & 15;
+    const int u = blockIdx.x;
+
+    // Q operand: query m16, dims 8g..8g+7 and 32+8g..32+8g+7 (zero past G).
+    uint4 qlo = make_uint4(0, 0, 0, 0), qhi = qlo;
+    if (m16 < G) {
+        const uint4* p = reinterpret_cast<const uint4*>(q_gen + ((size_t)u * G + m16) * kD);
+        qlo = p[g];
+        qhi = p[4 + g];
+    }
+    const bf16x8_t qa0 = __builtin_bit_cast(bf16x8_t, qlo);
+    const bf16x8_t qa1 = __builtin_bit_cast(bf16x8_t, qhi);
+    const uint16_t* K = k_full + (size_t)u * N * kD;
+
+    // Every tile's key rows are requested before the first MFMA; a key past
+    // N (partial or missing tile) reads row 0 and is masked below.
+    uint4 kr[TPW][2];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        const int key = 16 * (w + W * k) + m16;
+        const uint4* p = reinterpret_cast<const uint4*>(K + (size_t)(key < N ? key : 0) * kD);
+        kr[k][0] = p[g];
+        kr[k][1] = p[4 + g];
+    }
+    // s[k][i] = scale_log2 * S[query 4g+i][key 16 (w + W k) + m16]
+    f32x4_t s[TPW];
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, __builtin_bit_cast(bf16x8_t, kr[k][0]),
+                                                      acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1, __builtin_bit_cast(bf16x8_t, kr[k][1]),
+                                                      acc, 0, 0, 0);
+        const bool ok = 16 * (w + W * k) + m16 < N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[k][i] = ok ? acc[i] * scale_log2 : -INFINITY;
+            mx[i] = fmaxf(mx[i], s[k][i]);
+        }
+    }
+    // Row maxima over all N keys (finite: key 0 is in wave 0's first tile).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], o, kWave));
+    }
+    if constexpr (W > 1) {
+        if (m16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[0][w][4 * g + i] = mx[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float m = red[0][0][4 * g + i];
+#pragma unroll
+            for (int v = 1; v < W; ++v) m = fmaxf(m, red[0][v][4 * g + i]);
+            mx[i] = m;
+        }
+    }
+    // Probabilities (unnormalised) in place, and the row sums.
+    float l[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < TPW; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[k][i] = __builtin_amdgcn_exp2f(s[k][i] - mx[i]);
+            l[i] += s[k][i];
+        }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) l[i] += __shfl_xor(l[i], o, kWave);
+    }
+    if constexpr (W > 1) {
+        if (m16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[1][w][4 * g + i] = l[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float t = red[1][0][4 * g + i];
+#pragma unroll
+            for (int v = 1; v < W; ++v) t += red[1][v][4 * g + i];
+            l[i] = t;
+        }
+    }
+    float inv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) inv[i] = (4 * g + i < G) ? 1.f / l[i] : 0.f;  // padded queries add 0
+    // Per key: the normalised probabilities summed over the queries.
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        float col = s[k][0] * inv[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) col += s[k][i] * inv[i];
+        col += __shfl_xor(col, 16, kWave);
+        col += __shfl_xor(col, 32, kWave);
+        const int key = 16 * (w + W * k) + m16;
+        if (g == 0 && key < N) ws[(size_t)u * N + key] = col;
+    }
+}
+
 __device__ __forceinline__ uint64_t rank_key(float s, int j) {
     const uint32_t u = __float_as_uint(s);
     const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -320,8 +445,14 @@ __device__ __forceinline__ uint64_t rank_key(float s, int j) {
 // tokens in (score descending, index ascending) order.  Each wave ranks
 // tokens w, w + kSelWaves, ...; lane l holds keys l, l + 64, ... and one
 // ballot per 64 keys counts the larger ones.
+// NB > 0 (N <= 64 NB <= 512, one token per thread): all keys sit in NB
+// registers per lane, so the ballots need no bounds test; four tokens are
+// ranked per step, which keeps four independent compare / count chains in
+// flight, and the ascending compaction takes its positions from a ballot
+// per wave.  NB == 0 is the general form for longer sequences.
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
+template <int NB>
 __global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ gp_idx, int ld_gp, int n_gp, int K,
     float inv_hg, float* __restrict__ scores, int32_t* __restrict__ active_idx, int ld_act,
@@ -364,6 +495,66 @@ __global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
         keys[j] = (state[j] == 0) ? rank_key(s, j) : 0ull;
     }
     __syncthreads();
+
+    int32_t* crow = cached_idx + (size_t)b * ld_cached;
+    if constexpr (NB > 0) {
+        uint64_t kr[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int i = lane + kWave * k;
+            kr[k] = (i < N) ? keys[i] : 0ull;  // 0 is never larger than an eligible key
+        }
+        // Lane l holds the key of token wu + kSelWaves * l.  Tokens at or past
+        // N read key 0 and are skipped like ineligible ones; nt <= 64, so the
+        // lane index of every step stays below 64.
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        const int jl = wu + kSelWaves * lane;
+        const uint64_t kl = (jl < N) ? keys[jl] : 0ull;
+        const int nt = (N - wu + kSelWaves - 1) / kSelWaves;
+        for (int e0 = 0; e0 < nt; e0 += 4) {
+            uint64_t kj[4];
+            int cnt[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(kl), e0 + q);
+                const uint32_t hi =
+                    __builtin_amdgcn_readlane(static_cast<uint32_t>(kl >> 32), e0 + q);
+                kj[q] = (static_cast<uint64_t>(hi) << 32) | lo;
+                cnt[q] = 0;
+            }
+#pragma unroll
+            for (int k = 0; k < NB; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cnt[q] += __popcll(__ballot(kr[k] > kj[q]));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (kj[q] != 0 && cnt[q] < K && lane == 0) {
+                    const int j = wu + kSelWaves * (e0 + q);
+                    arow[n_gp + cnt[q]] = j;
+                    state[j] = 2;
+                }
+        }
+        __syncthreads();
+
+        // Ascending compaction: thread tid holds token tid.
+        const bool c = tid < N && state[tid] == 0;
+        const uint64_t m = __ballot(c);
+        const int below = __builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+        if (lane == 0) scan_scratch[w] = __popcll(m);
+        __syncthreads();
+        int pos = below, total = 0;
+#pragma unroll
+        for (int v = 0; v < kSelWaves; ++v) {
+            const int sv = scan_scratch[v];
+            pos += (v < w) ? sv : 0;
+            total += sv;
+        }
+        if (c && pos < ld_cached) crow[pos] = tid;
+        for (int t = total + tid; t < ld_cached; t += kSelThreads) crow[t] = -1;
+        if (tid == 0) cached_len[b] = total;
+        return;
+    }
 
     // The first kRegs * 64 keys live in registers; keys past them (N > 512)
     // are read from LDS in the counting loop.
@@ -413,7 +604,6 @@ __global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
     for (int j = j0; j < j1; ++j) cnt += (state[j] == 0);
     int total = 0;
     int pos = block_exclusive_scan<kSelThreads>(cnt, scan_scratch, &total);
-    int32_t* crow = cached_idx + (size_t)b * ld_cached;
     for (int j = j0; j < j1; ++j)
         if (state[j] == 0) {
             if (pos < ld_cached) crow[pos] = j;
@@ -440,7 +630,11 @@ int launch_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp
         const uint16_t* k = static_cast<const uint16_t*>(k_full);
         const int NS = N + 16;
         const size_t lds_s = (size_t)qt * 16 * NS * sizeof(float);
-        if (lds_s <= kMaxScoreLds) {
+        if (qt == 1 && (N + 15) / 16 <= kRegTiles * kRegWaves) {
+            hipLaunchKernelGGL((refresh_scores_reg_kernel<kRegTiles, kRegWaves>), grid,
+                               dim3(kRegWaves * kWave), 0, stream, q, k, workspace, G, N,
+                               scale_log2);
+        } else if (lds_s <= kMaxScoreLds) {
             switch (qt) {
                 case 1: hipLaunchKernelGGL(refresh_scores_lds_kernel<1>, grid, block, lds_s, stream, q, k, workspace, G, N, NS, scale_log2); break;
                 case 2: hipLaunchKernelGGL(refresh_scores_lds_kernel<2>, grid, block, lds_s, stream, q, k, workspace, G, N, NS, scale_log2); break;
@@ -464,9 +658,22 @@ int launch_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp
     if (st != MAR_OK) return st;
     const size_t lds2 = (size_t)N * sizeof(uint64_t) + (size_t)N;
     const float inv_hg = 1.f / (float)(H * G);
-    hipLaunchKernelGGL(refresh_select_kernel, dim3(B), dim3(kSelThreads), lds2, stream, workspace,
-                       gp_idx, ld_gp, n_gp, K, inv_hg, scores, active_idx, ld_act, cached_idx,
-                       ld_cached, cached_len, H, N);
+#define MARCA_SELECT(NB)                                                                     \
+    hipLaunchKernelGGL(refresh_select_kernel<NB>, dim3(B), dim3(kSelThreads), lds2, stream,     \
+                       workspace, gp_idx, ld_gp, n_gp, K, inv_hg, scores, active_idx, ld_act,   \
+                       cached_idx, ld_cached, cached_len, H, N)
+    switch ((N + kWave - 1) / kWave) {
+        case 1: MARCA_SELECT(1); break;
+        case 2: MARCA_SELECT(2); break;
+        case 3: MARCA_SELECT(3); break;
+        case 4: MARCA_SELECT(4); break;
+        case 5: MARCA_SELECT(5); break;
+        case 6: MARCA_SELECT(6); break;
+        case 7: MARCA_SELECT(7); break;
+        case 8: MARCA_SELECT(8); break;
+        default: MARCA_SELECT(0); break;
+    }
+#undef MARCA_SELECT
     return status_from_launch();
 }
 

@@ -127,7 +127,11 @@ def check_topk(q, k, gp, scores, act, cac, clen, K):
     (3, 2, 5, 70, 9, 7, "bf16"), (2, 3, 1, 33, 0, 4, "f32"), (2, 2, 16, 320, 32, 16, "bf16"),
     (2, 2, 17, 100, 20, 30, "bf16"), (1, 4, 40, 257, 60, 40, "f32"), (2, 1, 3, 64, 10, 0, "bf16"),
     (2, 2, 26, 1088, 52, 76, "bf16"), (1, 2, 64, 200, 10, 20, "bf16"),
-    (1, 2, 64, 300, 10, 20, "bf16")])
+    (1, 2, 64, 300, 10, 20, "bf16"),
+    # the register-resident scores take up to 16 queries and 320 keys; the
+    # selection keeps up to 512 keys in registers, past that it reads LDS
+    (2, 2, 16, 319, 32, 16, "bf16"), (2, 2, 16, 321, 32, 16, "bf16"),
+    (2, 2, 16, 500, 40, 25, "bf16"), (2, 2, 12, 700, 30, 40, "bf16")])
 def test_topk_small(marca, B, H, G, N, n_gp, K, dtype):
     out = topk_case(marca, B, H, G, N, n_gp, K, dtype, seed=B * 100 + N)
     check_topk(*out, K)
