@@ -506,15 +506,34 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
                     const_cast<uint16_t*>(kc_u), 0, N * kD * 2, 0x00020000);
                 const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
                     const_cast<uint16_t*>(vc_u), 0, N * kD * 2, 0x00020000);
+                // The K pieces are held in the MFMA operand layout: lane (g, m16)
+                // has pieces g and 4 + g of row 16t + m16, so storing either
+                // register would write half of each of 16 rows.  Exchanging the
+                // upper 8 lanes' first register with the lower 8 lanes' second
+                // one within each 16-lane row (DPP row shifts by 8 under a bank
+                // mask) gives one register with rows 16t..16t+7 and one with
+                // rows 16t+8..16t+15, each whole: every store then writes 8
+                // complete 128-byte rows, like the V stores below.
+                const int kpiece = (m16 < 8) ? g : 4 + g;
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const int r = c * kChunk + 16 * t + m16;
-                    const int n = (r >= An) ? -1 : (DENSE && active_idx == nullptr) ? r : aidx_s[r];
-                    const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.k[t][0]),
-                                                           rk, off + 16 * g, 0, kNT);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.k[t][1]),
-                                                           rk, off + 16 * (4 + g), 0, kNT);
+                    const u32x4_t k0 = __builtin_bit_cast(u32x4_t, ch.k[t][0]);
+                    const u32x4_t k1 = __builtin_bit_cast(u32x4_t, ch.k[t][1]);
+                    u32x4_t rows[2];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        // lanes 8..15 take k1 of lane - 8; lanes 0..7 keep k0
+                        rows[0][d] = __builtin_amdgcn_update_dpp(k0[d], k1[d], 0x118, 0xf, 0xc, false);
+                        // lanes 0..7 take k0 of lane + 8; lanes 8..15 keep k1
+                        rows[1][d] = __builtin_amdgcn_update_dpp(k1[d], k0[d], 0x108, 0xf, 0x3, false);
+                    }
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int r = c * kChunk + 16 * t + 8 * h + (m16 & 7);
+                        const int n = (r >= An) ? -1 : (DENSE && active_idx == nullptr) ? r : aidx_s[r];
+                        const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
+                        __builtin_amdgcn_raw_buffer_store_b128(rows[h], rk, off + 16 * kpiece, 0, kNT);
+                    }
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
