@@ -77,7 +77,10 @@ def small(dtype, B, H, N, A, seed):
 
 @pytest.mark.parametrize("dtype,A,Nc", [("bf16", 16, 48), ("bf16", 48, 272), ("bf16", 33, 1),
                                         ("bf16", 100, 37), ("bf16", 128, 160), ("bf16", 8, 50),
-                                        ("f32", 24, 40), ("bf16", 64, 0)])
+                                        ("f32", 24, 40), ("bf16", 64, 0),
+                                        # the K rows are stored 8 whole rows at a time:
+                                        # 21 active rows end inside such a group
+                                        ("bf16", 21, 11)])
 def test_fused_update_matches_attention_and_scatter(marca, dtype, A, Nc):
     cfg = small(dtype, 2, 3, A + Nc + 3, A, seed=900 + A + Nc)
     x = attention_inputs(cfg, DEV, ascending=False)
@@ -107,7 +110,9 @@ def test_fused_update_full_size_mar_l(marca):
 
 @pytest.mark.parametrize("dtype,B,H,N", [("bf16", 2, 3, 320), ("bf16", 2, 3, 200),
                                          ("bf16", 3, 2, 77), ("bf16", 2, 2, 8),
-                                         ("f32", 2, 2, 40), ("bf16", 128, 16, 320)])
+                                         ("f32", 2, 2, 40), ("bf16", 128, 16, 320),
+                                         # up to 64 tokens: the one-wave kernel, rows r -> r
+                                         ("bf16", 2, 3, 40), ("bf16", 3, 2, 61)])
 def test_fused_full_refresh(marca, dtype, B, H, N):
     """No active list: a refresh step's full attention over all N tokens and the
     rewrite of every cache row, in one call.  The output equals the plain full
