@@ -445,12 +445,12 @@ __device__ __forceinline__ uint64_t rank_key(float s, int j) {
 // tokens in (score descending, index ascending) order.  Each wave ranks
 // tokens w, w + kSelWaves, ...; lane l holds keys l, l + 64, ... and one
 // ballot per 64 keys counts the larger ones.
-// NB > 0 (N <= 64 NB <= 512, one token per thread): all keys sit in NB
+// NB > 0 (N <= 64 NB <= 512, at most one token per thread): all keys sit in NB
 // registers per lane, so the ballots need no bounds test; four tokens are
 // ranked per step, which keeps four independent compare / count chains in
 // flight, and the ascending compaction takes its positions from a ballot
 // per wave.  NB == 0 is the general form for longer sequences.
-constexpr int kSelThreads = 512;
+constexpr int kSelThreads = 1024;  // 16 waves: more compare / count chains in flight per CU
 constexpr int kSelWaves = kSelThreads / kWave;
 template <int NB>
 __global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
