@@ -53,3 +53,29 @@ def test_traffic_only_for_the_measured_source(tmp_path):
     os.remove(rec)
     assert b.load_traffic(1) is None
 
+
+
+def test_headline_record_contract():
+    """The fields the one-line record must carry, their types, and the value
+    and roofline arithmetic, at the MAR-L step shape with made-up timings."""
+    b = load_bench()
+    from mar_workloads import CONFIGS
+    cfg = CONFIGS["mar_l"]
+    cpu = {"value": 1.0, "unit": "tok/s", "cores": 16, "kind": "oracle", "sample": "s"}
+    rec = b.headline_record(cfg, 30, 100, 10, 1.5, 5400.0, 1.9e8, cpu)
+    required = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"}
+    assert required <= set(rec)
+    assert rec["n_gpus"] == 1 and rec["steps"] == 100 and rec["warmup"] == 10
+    assert rec["higher_is_better"] is True and rec["scaling"] == "weak"
+    assert rec["vs_baseline"] is None and rec["dtype"] == "bf16" and rec["unit"] == "tok/s"
+    # 128 sequences x 48 active queries x 30 layers per 1.5 ms step
+    assert rec["value"] == 128 * 48 * 30 / 1.5e-3
+    assert rec["config"]["workload"] == "mar_l_decode_step" and "model" not in rec["config"]
+    r = rec["roofline"]
+    assert set(r) == {"bound", "achieved", "peak", "unit", "frac", "traffic"}
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert r["frac"] == 5400.0 / 8000.0 and r["traffic"] == 1.9e8
+    assert rec["cpu_baseline"] is cpu
+    json.dumps(rec)  # serialisable as one line
