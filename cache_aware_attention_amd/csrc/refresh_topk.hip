@@ -452,6 +452,10 @@ __device__ __forceinline__ uint64_t rank_key(float s, int j) {
 // per wave.  NB == 0 is the general form for longer sequences.
 constexpr int kSelThreads = 1024;  // 16 waves: more compare / count chains in flight per CU
 constexpr int kSelWaves = kSelThreads / kWave;
+// NB <= 8 register blocks cover up to 512 tokens: with at least 512 threads
+// each token has a thread in the compaction, and with at least 8 waves each
+// wave ranks at most 64 tokens (one per lane) in the ranking loop.
+static_assert(kSelThreads >= 8 * kWave, "selection: the register-block path needs 512 threads");
 template <int NB>
 __global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ gp_idx, int ld_gp, int n_gp, int K,
