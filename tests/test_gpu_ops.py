@@ -131,7 +131,10 @@ def check_topk(q, k, gp, scores, act, cac, clen, K):
     # the register-resident scores take up to 16 queries and 320 keys; the
     # selection keeps up to 512 keys in registers, past that it reads LDS
     (2, 2, 16, 319, 32, 16, "bf16"), (2, 2, 16, 321, 32, 16, "bf16"),
-    (2, 2, 16, 500, 40, 25, "bf16"), (2, 2, 12, 700, 30, 40, "bf16")])
+    (2, 2, 16, 500, 40, 25, "bf16"), (2, 2, 12, 700, 30, 40, "bf16"),
+    # one token (every other key of the only tile masked; its score is 1) and one
+    # token past a whole tile
+    (1, 2, 4, 1, 0, 1, "bf16"), (2, 2, 16, 17, 0, 5, "bf16")])
 def test_topk_small(marca, B, H, G, N, n_gp, K, dtype):
     out = topk_case(marca, B, H, G, N, n_gp, K, dtype, seed=B * 100 + N)
     check_topk(*out, K)
