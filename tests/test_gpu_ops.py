@@ -208,6 +208,28 @@ def test_gate_small_bit_exact(marca, dtype):
     assert (reuse.cpu().numpy()[away] == r_ref[away]).all()
 
 
+@pytest.mark.parametrize("dtype,B,N,W", [
+    ("bf16", 2, 1, 8),      # one token of one 16-byte piece: only lane 0 holds data
+    ("f32", 2, 5, 4),
+    ("bf16", 3, 37, 520),   # 65 pieces: the second group of 64 holds one
+    ("bf16", 1, 300, 2048), # four pieces per lane
+])
+def test_gate_widths_and_lengths(marca, dtype, B, N, W):
+    x, y, rho = gate_features(B, N, W, seed=B * 1000 + N + W, device=DEV, dtype=dtype)
+    cos, reuse, cidx, clen = marca.mar_cos_gate(x, y, 0.95)
+    torch.cuda.synchronize()
+    c_gpu = cos.double().cpu().numpy()
+    tau32 = float(np.float32(0.95))
+    r2, c2, l2 = oracle.gate_from_cos(c_gpu, tau32)
+    assert (reuse.cpu().numpy() == r2).all() and (cidx.cpu().numpy() == c2).all()
+    assert (clen.cpu().numpy() == l2).all()
+    c_ref, r_ref, _, _ = oracle.cos_gate(x.double().cpu().numpy(), y.double().cpu().numpy(), tau32)
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert np.abs(c_gpu - c_ref).max() <= tol
+    away = np.abs(c_ref - tau32) > 1e-4
+    assert (reuse.cpu().numpy()[away] == r_ref[away]).all()
+
+
 def test_gate_near_threshold(marca):
     x, y, rho = gate_features(2, 300, 1024, seed=22, device=DEV, near_tau=0.95, near_width=1e-3)
     cos, reuse, cidx, clen = marca.mar_cos_gate(x, y, 0.95)
