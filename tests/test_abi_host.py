@@ -172,6 +172,18 @@ def test_plan_step_matches_oracle(lib, name):
                 assert bool(fl & _lib.MAR_LAYER_GATE) == S.gate_applies(ref, layer)
 
 
+def test_plan_step_budget_clamp_golden(lib, golden_dir):
+    """The library's planner on the hand-computed plans, including budgets that
+    exceed the tokens outside G and P (K clamped to the eligible tokens)."""
+    import json
+    with open(os.path.join(golden_dir, "schedule_budget_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        got = _lib.mar_plan_step(c["counts"], c["step"], c["n_tokens"], c["budget"], c["period"])
+        for k, v in c["plan"].items():
+            assert int(getattr(got, k)) == v, (c["why"], k)
+
+
 def test_plan_step_rejections(lib):
     plan = _lib.StepPlan()
     arr = (ctypes.c_int32 * 3)(1, 2, 3)

@@ -118,7 +118,8 @@ def test_gate_wide_features(marca):
     cos, reuse, cidx, clen = marca.mar_cos_gate(xc, yc, 0.95)
     torch.cuda.synchronize()
     c_ref, _, _, _ = oracle.cos_gate(f64(xc), f64(yc), 0.95)
-    assert np.abs(f64(cos) - c_ref).max() <= 2e-2
+    # the same bf16 values reduced in fp32 and fp64: chains of W/64 + 6 additions
+    assert np.abs(f64(cos) - c_ref).max() <= 1e-5
     r2, c2, l2 = oracle.gate_from_cos(f64(cos), np.float32(0.95))
     assert (reuse.cpu().numpy() == r2).all() and (cidx.cpu().numpy() == c2).all()
     assert (clen.cpu().numpy() == l2).all()

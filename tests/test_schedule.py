@@ -19,6 +19,19 @@ def test_refresh_steps_golden(golden_dir):
     assert sum(not p.refresh for p in plans) == g["n_cache_aware"]
 
 
+def test_budget_clamp_golden(golden_dir):
+    """Hand-computed plans, including budgets larger than the tokens left once
+    G and P are taken, where K is clamped to the eligible tokens."""
+    with open(os.path.join(golden_dir, "schedule_budget_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    assert sum(c["plan"]["n_refresh"] < c["budget"] - c["plan"]["n_gen"] - c["plan"]["n_prev"]
+               for c in cases) >= 3  # the upper clamp binds in at least three cases
+    for c in cases:
+        p = S.plan_step(c["counts"], c["step"], c["n_tokens"], c["budget"], c["period"])
+        for k, v in c["plan"].items():
+            assert int(getattr(p, k)) == v, (c["why"], k)
+
+
 def test_cosine_counts():
     for n_img, steps in [(256, 64), (1024, 64), (256, 16), (64, 64)]:
         c = cosine_counts(n_img, steps)
