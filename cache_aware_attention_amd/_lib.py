@@ -25,6 +25,7 @@ MAR_CFG_REUSE = 1
 MAR_LAYER_CACHE = 1
 MAR_LAYER_SELECT = 2
 MAR_LAYER_GATE = 4
+MAR_REFRESH_TOPK_SCRATCH_BYTES = 8 << 20
 
 
 class MarError(RuntimeError):
@@ -73,6 +74,9 @@ def load_library(path: Optional[str] = None):
     lib.mar_refresh_topk.restype = I
     lib.mar_refresh_topk.argtypes = [V, V, V, I, I, I, F, V, V, I, V, I, V, V, S, I, I, I, I, I,
                                      I, V]
+    lib.mar_refresh_topk_noalloc.restype = I
+    lib.mar_refresh_topk_noalloc.argtypes = [V, V, V, I, I, I, F, V, V, I, V, I, V, I, I, I, I,
+                                             I, I, V]
     lib.mar_cos_gate.restype = I
     lib.mar_cos_gate.argtypes = [V, V, F, F, V, V, V, V, I, I, I, I, V]
     lib.mar_cfg_residual.restype = I
@@ -269,8 +273,10 @@ def mar_refresh_topk_workspace(B: int, H: int, N: int) -> int:
 
 
 def mar_refresh_topk(q_gen, k_full, gp_idx, n_gp, K, scores=None, active_idx=None,
-                     cached_idx=None, cached_len=None, workspace=None, scale=None, stream=None):
-    """Returns (scores [B,N], active_idx [B,ld_act], cached_idx [B,ld_cached], cached_len [B])."""
+                     cached_idx=None, cached_len=None, workspace=None, scale=None, stream=None,
+                     _noalloc=False):
+    """Returns (scores [B,N], active_idx [B,ld_act], cached_idx [B,ld_cached], cached_len [B]).
+    With _noalloc the call goes to mar_refresh_topk_noalloc (no workspace)."""
     B, H, G, D = q_gen.shape
     N = k_full.shape[2]
     dt = q_gen.dtype
@@ -294,7 +300,7 @@ def mar_refresh_topk(q_gen, k_full, gp_idx, n_gp, K, scores=None, active_idx=Non
     if cached_len is None:
         cached_len = torch.empty((B,), dtype=torch.int32, device=dev)
     ws_bytes = mar_refresh_topk_workspace(B, H, N)
-    if workspace is None:
+    if workspace is None and not _noalloc:
         workspace = torch.empty((ws_bytes // 4,), dtype=torch.float32, device=dev)
     _dev(scores, "scores", torch.float32, (B, N))
     _dev(cached_len, "cached_len", torch.int32, (B,))
@@ -303,6 +309,15 @@ def mar_refresh_topk(q_gen, k_full, gp_idx, n_gp, K, scores=None, active_idx=Non
         if not gp_idx.is_cuda or gp_idx.dtype != torch.int32:
             raise ValueError("gp_idx must be a GPU int32 tensor")
         gp_ptr = ctypes.c_void_p(gp_idx.data_ptr())
+    if _noalloc:
+        st = load_library().mar_refresh_topk_noalloc(
+            _dev(q_gen, "q_gen"), _dev(k_full, "k_full"), gp_ptr, ld_gp, int(n_gp), int(K),
+            float(D ** -0.5 if scale is None else scale), _dev(scores, "scores"),
+            _dev(active_idx, "active_idx", torch.int32), active_idx.shape[1],
+            _dev(cached_idx, "cached_idx", torch.int32), cached_idx.shape[1],
+            _dev(cached_len, "cached_len"), B, H, G, N, D, code, _stream(stream))
+        _check("mar_refresh_topk_noalloc", st)
+        return scores, active_idx, cached_idx, cached_len
     st = load_library().mar_refresh_topk(
         _dev(q_gen, "q_gen"), _dev(k_full, "k_full"), gp_ptr, ld_gp, int(n_gp), int(K),
         float(D ** -0.5 if scale is None else scale), _dev(scores, "scores"),
@@ -312,6 +327,15 @@ def mar_refresh_topk(q_gen, k_full, gp_idx, n_gp, K, scores=None, active_idx=Non
         workspace.numel() * workspace.element_size(), B, H, G, N, D, code, _stream(stream))
     _check("mar_refresh_topk", st)
     return scores, active_idx, cached_idx, cached_len
+
+
+def mar_refresh_topk_noalloc(q_gen, k_full, gp_idx, n_gp, K, scores=None, active_idx=None,
+                             cached_idx=None, cached_len=None, scale=None, stream=None):
+    """mar_refresh_topk through the allocation-free entry point: the library's
+    per-device array takes the partial scores.  Output tensors left as None
+    are allocated here by torch (pass them in to allocate nothing)."""
+    return mar_refresh_topk(q_gen, k_full, gp_idx, n_gp, K, scores, active_idx, cached_idx,
+                            cached_len, None, scale, stream, _noalloc=True)
 
 
 def mar_cos_gate(x_cur, x_cached, tau=0.95, eps=1e-8, cos_out=None, reuse_mask=None,

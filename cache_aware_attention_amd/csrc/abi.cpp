@@ -121,12 +121,12 @@ extern "C" size_t mar_refresh_topk_workspace(int B, int H, int N) {
     return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
-extern "C" int mar_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp_idx,
-                                int ld_gp, int n_gp, int K, float scale, float* scores,
-                                int32_t* active_idx, int ld_act, int32_t* cached_idx,
-                                int ld_cached, int32_t* cached_len, void* workspace,
-                                size_t ws_bytes, int B, int H, int G, int N, int D, int dtype,
-                                void* stream) {
+// Checks shared by both top-K entry points (everything but the workspace).
+static int check_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp_idx,
+                              int ld_gp, int n_gp, int K, float scale, const float* scores,
+                              const int32_t* active_idx, int ld_act, const int32_t* cached_idx,
+                              int ld_cached, const int32_t* cached_len, int B, int H, int G,
+                              int N, int D, int dtype) {
     if (!q_gen || !k_full || !scores || !active_idx || !cached_idx || !cached_len)
         return MAR_E_NULL;
     if (n_gp > 0 && !gp_idx) return MAR_E_NULL;
@@ -140,12 +140,41 @@ extern "C" int mar_refresh_topk(const void* q_gen, const void* k_full, const int
     if (D != kHeadDim || N > kMaxTopkTokens) return MAR_E_UNSUPPORTED;
     if (!(scale == scale)) return MAR_E_RANGE;
     if (!aligned16(q_gen) || !aligned16(k_full)) return MAR_E_RANGE;
+    return MAR_OK;
+}
+
+extern "C" int mar_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp_idx,
+                                int ld_gp, int n_gp, int K, float scale, float* scores,
+                                int32_t* active_idx, int ld_act, int32_t* cached_idx,
+                                int ld_cached, int32_t* cached_len, void* workspace,
+                                size_t ws_bytes, int B, int H, int G, int N, int D, int dtype,
+                                void* stream) {
+    const int st = check_refresh_topk(q_gen, k_full, gp_idx, ld_gp, n_gp, K, scale, scores,
+                                      active_idx, ld_act, cached_idx, ld_cached, cached_len, B,
+                                      H, G, N, D, dtype);
+    if (st != MAR_OK) return st;
     if (!workspace) return MAR_E_WORKSPACE;
     if (ws_bytes < mar_refresh_topk_workspace(B, H, N)) return MAR_E_WORKSPACE;
     if (!aligned16(workspace)) return MAR_E_RANGE;
     return marca::launch_refresh_topk(q_gen, k_full, gp_idx, ld_gp, n_gp, K, scale, scores,
                                       active_idx, ld_act, cached_idx, ld_cached, cached_len,
                                       static_cast<float*>(workspace), B, H, G, N, dtype, stream);
+}
+
+extern "C" int mar_refresh_topk_noalloc(const void* q_gen, const void* k_full,
+                                        const int32_t* gp_idx, int ld_gp, int n_gp, int K,
+                                        float scale, float* scores, int32_t* active_idx,
+                                        int ld_act, int32_t* cached_idx, int ld_cached,
+                                        int32_t* cached_len, int B, int H, int G, int N, int D,
+                                        int dtype, void* stream) {
+    const int st = check_refresh_topk(q_gen, k_full, gp_idx, ld_gp, n_gp, K, scale, scores,
+                                      active_idx, ld_act, cached_idx, ld_cached, cached_len, B,
+                                      H, G, N, D, dtype);
+    if (st != MAR_OK) return st;
+    if (mar_refresh_topk_workspace(B, H, N) > marca::kTopkScratchBytes) return MAR_E_WORKSPACE;
+    return marca::launch_refresh_topk_noalloc(q_gen, k_full, gp_idx, ld_gp, n_gp, K, scale,
+                                              scores, active_idx, ld_act, cached_idx, ld_cached,
+                                              cached_len, B, H, G, N, dtype, stream);
 }
 
 extern "C" int mar_cos_gate(const void* x_cur, const void* x_cached, float tau, float eps,

@@ -6,6 +6,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "mar_cache_attn.h"
+
 namespace marca {
 
 int launch_cache_attn(const void* q_a, const void* k_a, const void* v_a,
@@ -36,6 +38,16 @@ int launch_refresh_topk(const void* q_gen, const void* k_full,
                         int32_t* cached_idx, int ld_cached, int32_t* cached_len,
                         float* workspace, int B, int H, int G, int N, int dtype,
                         void* stream);
+
+// The allocation-free top-K: the partial scores go to the library's own
+// per-device array of kTopkScratchBytes (B*H*N floats must fit; checked by
+// the caller).
+constexpr size_t kTopkScratchBytes = MAR_REFRESH_TOPK_SCRATCH_BYTES;
+int launch_refresh_topk_noalloc(const void* q_gen, const void* k_full,
+                                const int32_t* gp_idx, int ld_gp, int n_gp, int K, float scale,
+                                float* scores, int32_t* active_idx, int ld_act,
+                                int32_t* cached_idx, int ld_cached, int32_t* cached_len,
+                                int B, int H, int G, int N, int dtype, void* stream);
 
 int launch_cos_gate(const void* x_cur, const void* x_cached, float tau, float eps,
                     float* cos_out, uint8_t* reuse_mask, int32_t* compute_idx,

@@ -22,6 +22,8 @@
 // ~index, so equal scores put the lower index first), emits the refreshing
 // tokens, and
 // compacts the ascending cached complement with a block prefix sum.
+#include <mutex>
+
 #include "device_util.h"
 #include "launch.h"
 
@@ -48,14 +50,14 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2)
 // fp32 version of kernel 1: plain FMA, one generating query at a time with
 // block-wide max and sum reductions (three sweeps over the head's keys per
 // query; this path serves float inputs, not the bf16 decoding shapes).
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* scratch) {
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red_s) {
     v = is_max ? wave_max(v) : wave_sum(v);
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     __syncthreads();
-    if (lane == 0) scratch[wid] = v;
+    if (lane == 0) red_s[wid] = v;
     __syncthreads();
-    float r = scratch[0];
-    for (int w = 1; w < kThreads / kWave; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
+    float r = red_s[0];
+    for (int w = 1; w < kThreads / kWave; ++w) r = is_max ? fmaxf(r, red_s[w]) : r + red_s[w];
     return r;
 }
 
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void refresh_scores_f32_kernel(
     const float* __restrict__ q_gen, const float* __restrict__ k_full, float* __restrict__ ws,
     int G, int N, float scale_log2) {
     __shared__ float q_s[kD];
-    __shared__ float scratch[kThreads / kWave];
+    __shared__ float red_s[kThreads / kWave];
     extern __shared__ float acc_s[];  // [N]
     const int tid = threadIdx.x;
     const int u = blockIdx.x;
@@ -88,10 +90,10 @@ __global__ __launch_bounds__(kThreads) void refresh_scores_f32_kernel(
         __syncthreads();
         float mloc = -INFINITY;
         for (int j = tid; j < N; j += kThreads) mloc = fmaxf(mloc, dot_row(q_s, K + (size_t)j * kD));
-        const float M = block_reduce(mloc, true, scratch);
+        const float M = block_reduce(mloc, true, red_s);
         float lloc = 0.f;
         for (int j = tid; j < N; j += kThreads) lloc += exp2f(dot_row(q_s, K + (size_t)j * kD) - M);
-        const float inv = 1.f / block_reduce(lloc, false, scratch);
+        const float inv = 1.f / block_reduce(lloc, false, red_s);
         for (int j = tid; j < N; j += kThreads)
             acc_s[j] += exp2f(dot_row(q_s, K + (size_t)j * kD) - M) * inv;
     }
@@ -679,6 +681,68 @@ int launch_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp
     }
 #undef MARCA_SELECT
     return status_from_launch();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free form (mar_refresh_topk_noalloc), for callers that cannot
+// allocate device memory.  The per-(sequence, head, token) partial scores go
+// to `scratch`, a file-scope device array of kTopkScratchBytes: each device
+// that runs the call holds its own copy at its own address until the process
+// ends.  In host code the array's name is only a host-side stand-in, so the
+// device address is looked up once per device with hipGetSymbolAddress (on
+// the device of the call's stream) and only that address is passed to the
+// kernels.  Every scores kernel writes each of the B*H*N partials before the
+// selection reads them, so the array needs no clearing between calls; calls
+// that overlap on one device share it and race.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) float scratch[kTopkScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+// The device address of `scratch` on the device of `stream` (the current
+// device for the null stream), looked up on the first call on that device.
+int scratch_address(hipStream_t stream, float** out) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return MAR_E_LAUNCH;
+    int dev = cur;
+    if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return MAR_E_LAUNCH;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return MAR_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return MAR_E_LAUNCH;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return MAR_E_LAUNCH;
+        }
+        g_scratch_dev[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return MAR_OK;
+}
+
+}  // namespace
+
+int launch_refresh_topk_noalloc(const void* q_gen, const void* k_full, const int32_t* gp_idx,
+                                int ld_gp, int n_gp, int K, float scale, float* scores,
+                                int32_t* active_idx, int ld_act, int32_t* cached_idx,
+                                int ld_cached, int32_t* cached_len, int B, int H, int G, int N,
+                                int dtype, void* stream_v) {
+    float* ws = nullptr;
+    const int st = scratch_address(static_cast<hipStream_t>(stream_v), &ws);
+    if (st != MAR_OK) return st;
+    return launch_refresh_topk(q_gen, k_full, gp_idx, ld_gp, n_gp, K, scale, scores, active_idx,
+                               ld_act, cached_idx, ld_cached, cached_len, ws, B, H, G, N, dtype,
+                               stream_v);
 }
 
 }  // namespace marca

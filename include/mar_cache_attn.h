@@ -18,7 +18,8 @@
  *     GPU work is queued; a failed check queues nothing.
  *   - Ownership: every buffer pointer is caller-owned device memory (the
  *     library never allocates, frees or retains buffers, and keeps no state
- *     between calls).  Host-side arguments are marked (host).
+ *     between calls; mar_refresh_topk_noalloc's own device array is the one
+ *     exception, described there).  Host-side arguments are marked (host).
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *     stream).  Calls are asynchronous on it; the caller synchronises.
  *   - Layouts: dense row-major; [B,H,N,D] means index ((b*H+h)*N+n)*D+d.
@@ -213,6 +214,34 @@ int mar_refresh_topk(const void* q_gen, const void* k_full,
                      int32_t* cached_idx, int ld_cached, int32_t* cached_len,
                      void* workspace, size_t ws_bytes,
                      int B, int H, int G, int N, int D, int dtype, void* stream);
+
+/*
+ * mar_refresh_topk without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, fixed serving loops,
+ * harnesses that forbid allocation.  It calls no hipMalloc, hipFree or
+ * allocating library routine.
+ *
+ * Arguments, outputs and errors as for mar_refresh_topk.  The per-(sequence,
+ * head, token) partial scores go to a device array inside the library of
+ * MAR_REFRESH_TOPK_SCRATCH_BYTES bytes, one per device, which each device the
+ * call runs on holds until the process ends; its address is looked up on the
+ * first call on a device (the device of `stream`, the current one for the
+ * null stream).  B*H*N*4 bytes must fit in it, else MAR_E_WORKSPACE and
+ * nothing is queued (8 MiB: e.g. 256 sequences x 20 heads x 320 tokens, or
+ * 64 x 16 x 1088).  Every call writes all the partials it reads, so no state
+ * carries over from one call to the next, but all calls on one device share
+ * the array: calls that overlap on one device (two streams, two host threads)
+ * race and give unspecified results.  MAR_E_LAUNCH if the runtime cannot give
+ * the array's address.
+ */
+#define MAR_REFRESH_TOPK_SCRATCH_BYTES ((size_t)8 << 20)
+int mar_refresh_topk_noalloc(const void* q_gen, const void* k_full,
+                             const int32_t* gp_idx, int ld_gp, int n_gp,
+                             int K, float scale,
+                             float* scores,
+                             int32_t* active_idx, int ld_act,
+                             int32_t* cached_idx, int ld_cached, int32_t* cached_len,
+                             int B, int H, int G, int N, int D, int dtype, void* stream);
 
 /*
  * Cosine-similarity token gate  ([LazyMAR] Key designs, token cache: in the

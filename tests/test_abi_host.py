@@ -137,6 +137,17 @@ def test_topk_rejections(lib):
     assert topk(lib, ws_bytes=100) == E_WS
 
 
+def test_refresh_topk_noalloc_rejections(lib):
+    f = lib.mar_refresh_topk_noalloc
+    # q, k, gp, ld_gp, n_gp, K, scale, scores, act, ld_act, cached, ld_cached, len, B, H, G, N, D, dt, s
+    assert f(None, P, P, 4, 4, 4, 0.125, P, P, 8, P, 320, P, 2, 2, 4, 320, 64, 1, None) == E_NULL
+    assert f(P, P, P, 4, 4, 400, 0.125, P, P, 404, P, 320, P, 2, 2, 4, 320, 64, 1, None) == E_RANGE
+    assert f(P, P, P, 4, 4, 4, 0.125, P, P, 8, P, 320, P, 2, 2, 4, 320, 32, 1, None) == E_UNSUP
+    # B*H*N floats beyond the library's 8 MiB array: refused before any GPU work
+    assert 1024 * 16 * 320 * 4 > _lib.MAR_REFRESH_TOPK_SCRATCH_BYTES
+    assert f(P, P, P, 4, 4, 4, 0.125, P, P, 8, P, 320, P, 1024, 16, 4, 320, 64, 1, None) == E_WS
+
+
 def test_gate_and_cfg_rejections(lib):
     g = lib.mar_cos_gate
     assert g(None, P, 0.95, 1e-8, P, P, P, P, 2, 10, 64, 1, None) == E_NULL
