@@ -207,6 +207,55 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // swizzled LDS tile.
 __device__ __forceinline__ int swz(int r, int piece) { return r * 128 + ((piece ^ (r & 7)) << 4); }
 
+// Streaming 16-byte load (nontemporal: the line is not kept for reuse).  On
+// this chip such loads sustain more HBM read bandwidth than plain loads for
+// data that is read once, as every K/V row of the attention is.
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// Cache-policy bits of a streaming (nontemporal) buffer load or store.
+constexpr int kStreamPolicy = 2;
+
+// Buffer resource over `bytes` bytes at p (raw buffer, range-checked: an
+// offset at or past `bytes` reads zero / drops the store).  p and bytes are
+// wave-uniform; taking them through readfirstlane keeps the descriptor in
+// scalar registers.  A pointer the compiler also holds in vector registers
+// (for per-lane address selects) would otherwise make every buffer access a
+// readfirstlane loop behind a wait for all outstanding loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    void* q = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Two layouts of 16 rows x 128 bytes held in two 16-byte registers per lane
+// (lane (g, m16): g = lane / 16, m16 = lane % 16):
+//  * operand layout (A/B operand of v_mfma_f32_16x16x32_bf16 over 64 head
+//    dims): x0 = piece g and x1 = piece 4 + g of row m16;
+//  * whole-row layout: r_h = piece (m16 < 8 ? g : 4 + g) of row 8h + m16 % 8,
+//    so one register of the 64 lanes covers 8 complete rows.
+// A load or store of whole rows moves complete 128-byte lines (a streaming
+// load of half-rows fetches each line twice).  Each direction exchanges the
+// upper 8 lanes' first register with the lower 8 lanes' second one within
+// each 16-lane row: two DPP row shifts by 8 per dword, under bank masks.
+__device__ __forceinline__ void swap_row_halves(uint4 a, uint4 b, uint4& x, uint4& y) {
+    const u32x4_t a4 = __builtin_bit_cast(u32x4_t, a);
+    const u32x4_t b4 = __builtin_bit_cast(u32x4_t, b);
+    u32x4_t xo, yo;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        // lanes 8..15 of each row take b of lane - 8; lanes 0..7 keep a
+        xo[d] = __builtin_amdgcn_update_dpp(a4[d], b4[d], 0x118, 0xf, 0xc, false);
+        // lanes 0..7 take a of lane + 8; lanes 8..15 keep b
+        yo[d] = __builtin_amdgcn_update_dpp(b4[d], a4[d], 0x108, 0xf, 0x3, false);
+    }
+    x = __builtin_bit_cast(uint4, xo);
+    y = __builtin_bit_cast(uint4, yo);
+}
+
 // Transposing 8-byte LDS read (ds_read_b64_tr_b16): within each 16-lane
 // group, lane i receives element (i mod 4) of the 8-byte chunk addressed by
 // lane 4e + i/4 of the group, for e = 0..3.
@@ -225,25 +274,24 @@ __device__ __forceinline__ float max_over_groups(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Row r of the virtual sequence [active ; cached] of one unit: a pointer to
-// its 64 elements and whether it exists.  Missing rows point at active row 0.
-__device__ __forceinline__ const uint16_t* row_ptr(int r, int A, int Nc, const int32_t* cidx_s,
-                                                   const uint16_t* base_a,
-                                                   const uint16_t* base_c, bool& ok) {
+// Row r of the virtual sequence [active ; cached] of one unit: its element
+// offset in the active block (is_c false) or the unit's cache rows (is_c
+// true), and whether it exists.  Missing rows are active row 0.
+__device__ __forceinline__ int row_ofs(int r, int A, int Nc, const int32_t* cidx_s, bool& is_c,
+                                       bool& ok) {
     const int c = r - A;
     const bool is_a = r < A;
     const bool in_c = static_cast<unsigned>(c) < static_cast<unsigned>(Nc);
     const int n = cidx_s[in_c ? c : 0];  // the list area holds at least one entry
     ok = is_a || (in_c && n >= 0);
-    const uint16_t* pc = base_c + static_cast<size_t>(n >= 0 ? n : 0) * kD;
-    const uint16_t* pa = base_a + static_cast<size_t>(is_a ? r : 0) * kD;
-    return (!is_a && ok) ? pc : pa;
+    is_c = !is_a && ok;
+    return (is_c ? n : (is_a ? r : 0)) * kD;
 }
 
 // Registers of one chunk in flight.
 struct ChunkRegs {
-    uint4 k[2][2];   // K operand pieces: rows 16t + m16, pieces g and 4+g
-    uint4 v[4];      // V rows 8k + lane/8, piece lane%8
+    uint4 k[2][2];   // K rows 16t..16t+15 in the whole-row layout (see swap_row_halves)
+    uint4 v[4];      // V in the same layout: piece kpiece of row 8k + m16 % 8
     uint32_t valid;  // bit j: key row j of the chunk exists (wave-uniform)
 };
 
@@ -334,12 +382,9 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         ce = min(cb + per, nchunks);
     }
     static_assert(!DENSE || !RAGGED, "dense rows: uniform counts only");
-    const __amdgpu_buffer_rsrc_t rka = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(ka_u), 0, An * kD * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rva = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(va_u), 0, An * kD * 2, 0x00020000);
-    const int k_lofs = m16 * (kD * 2) + 16 * g;                 // K: row m16, piece g
-    const int v_lofs = (lane >> 3) * (kD * 2) + 16 * (lane & 7);  // V: row lane/8, piece lane%8
+    const __amdgpu_buffer_rsrc_t rka = uniform_rsrc(ka_u, An * kD * 2);
+    const __amdgpu_buffer_rsrc_t rva = uniform_rsrc(va_u, An * kD * 2);
+    const int k_lofs = (m16 & 7) * (kD * 2) + 16 * ((m16 < 8) ? g : 4 + g);  // K: whole rows
 
     // The first entries of the cached list are requested first: they gate
     // every chunk that holds a cached row.
@@ -355,13 +400,23 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     // Q tile as the B operand of S^T = K Q^T: lane holds query m16 of tile qt,
     // head dims [8g, 8g+8) (k-step 0) and [32+8g, 32+8g+8) (k-step 1).
     // Queries past the group's end load its last query; they are never stored.
+    // Loaded as whole rows (lane: piece kpiece of query 16qt + 8h + m16 % 8)
+    // and exchanged into the operand layout.
+    const int kpiece = (m16 < 8) ? g : 4 + g;
     bf16x8_t qf[NQT][2];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-        const int qi = q0 + min(qt * 16 + m16, nq - 1);
-        const uint4* p = reinterpret_cast<const uint4*>(q_a + (static_cast<size_t>(u) * A + qi) * kD);
-        qf[qt][0] = as_bf16x8(p[g]);
-        qf[qt][1] = as_bf16x8(p[4 + g]);
+        uint4 qr[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int qi = q0 + min(qt * 16 + 8 * h + (m16 & 7), nq - 1);
+            qr[h] = ld_stream(reinterpret_cast<const uint4*>(
+                                  q_a + (static_cast<size_t>(u) * A + qi) * kD) + kpiece);
+        }
+        uint4 x, y;
+        swap_row_halves(qr[0], qr[1], x, y);
+        qf[qt][0] = as_bf16x8(x);
+        qf[qt][1] = as_bf16x8(y);
     }
 
     auto issue = [&](int c, ChunkRegs& cr) __attribute__((always_inline)) {
@@ -371,35 +426,37 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 cr.v[k] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rva, rb + v_lofs + 1024 * k, 0, 0));
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rva, rb + k_lofs + 1024 * k, 0, kStreamPolicy));
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                cr.k[t][0] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rka, rb + k_lofs + 2048 * t, 0, 0));
-                cr.k[t][1] = __builtin_bit_cast(
-                    uint4,
-                    __builtin_amdgcn_raw_buffer_load_b128(rka, rb + k_lofs + 2048 * t + 64, 0, 0));
-            }
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    cr.k[t][h] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rka, rb + k_lofs + 2048 * t + 1024 * h,
+                                                                     0, kStreamPolicy));
             cr.valid = 0;
             return;
         }
+        // K and V as whole rows at one row lookup per 8 rows: lane (g, m16)
+        // loads piece kpiece of row 8k + m16 % 8 (k = 2t + h for K); lanes
+        // 0..7 see rows 8k + 0..7.  V is requested first: it is consumed
+        // first (into LDS).
         uint32_t valid = 0;
+        int ofs[4];
+        bool cached[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {  // V first: it is consumed first (into LDS)
+        for (int k = 0; k < 4; ++k) {
             bool ok;
-            const uint4* p = reinterpret_cast<const uint4*>(
-                row_ptr(r0 + 8 * k + (lane >> 3), An, Ncn, cidx_s, va_u, vc_u, ok));
-            cr.v[k] = p[lane & 7];
+            ofs[k] = row_ofs(r0 + 8 * k + (m16 & 7), An, Ncn, cidx_s, cached[k], ok) + 8 * kpiece;
+            valid |= static_cast<uint32_t>(__ballot(ok) & 0xffull) << (8 * k);
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            bool ok;
-            const uint4* p = reinterpret_cast<const uint4*>(
-                row_ptr(r0 + 16 * t + m16, An, Ncn, cidx_s, ka_u, kc_u, ok));
-            cr.k[t][0] = p[g];
-            cr.k[t][1] = p[4 + g];
-            valid |= static_cast<uint32_t>(__ballot(ok) & 0xffffull) << (16 * t);
-        }
+        for (int k = 0; k < 4; ++k)
+            cr.v[k] = ld_stream(reinterpret_cast<const uint4*>((cached[k] ? vc_u : va_u) + ofs[k]));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            cr.k[k >> 1][k & 1] =
+                ld_stream(reinterpret_cast<const uint4*>((cached[k] ? kc_u : ka_u) + ofs[k]));
         cr.valid = valid;
     };
 
@@ -470,7 +527,7 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         for (int dt = 0; dt < 4; ++dt)
             vofs[h][dt] = swz(16 * h + 4 * g + (m16 >> 2), 2 * dt + ((m16 & 3) >> 1)) +
                           ((m16 & 1) << 3);
-    const int vst = swz(lane >> 3, lane & 7);  // V store slot, + 1024 per 8 rows
+    const int vst = swz(m16 & 7, kpiece);  // V store slot, + 1024 per 8 rows
 
     const float thr_raw = kRescaleLog2 / scale_log2;
     bool tile_on[NQT];
@@ -502,46 +559,21 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
                 // lane, skipped entry) is dropped by the range check.
                 constexpr uint32_t kSkip = 0x80000000u;
                 constexpr int kNT = 2;  // cache-policy bits: nontemporal (streaming) store
-                const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<uint16_t*>(kc_u), 0, N * kD * 2, 0x00020000);
-                const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<uint16_t*>(vc_u), 0, N * kD * 2, 0x00020000);
-                // The K pieces are held in the MFMA operand layout: lane (g, m16)
-                // has pieces g and 4 + g of row 16t + m16, so storing either
-                // register would write half of each of 16 rows.  Exchanging the
-                // upper 8 lanes' first register with the lower 8 lanes' second
-                // one within each 16-lane row (DPP row shifts by 8 under a bank
-                // mask) gives one register with rows 16t..16t+7 and one with
-                // rows 16t+8..16t+15, each whole: every store then writes 8
-                // complete 128-byte rows, like the V stores below.
-                const int kpiece = (m16 < 8) ? g : 4 + g;
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const u32x4_t k0 = __builtin_bit_cast(u32x4_t, ch.k[t][0]);
-                    const u32x4_t k1 = __builtin_bit_cast(u32x4_t, ch.k[t][1]);
-                    u32x4_t rows[2];
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        // lanes 8..15 take k1 of lane - 8; lanes 0..7 keep k0
-                        rows[0][d] = __builtin_amdgcn_update_dpp(k0[d], k1[d], 0x118, 0xf, 0xc, false);
-                        // lanes 0..7 take k0 of lane + 8; lanes 8..15 keep k1
-                        rows[1][d] = __builtin_amdgcn_update_dpp(k1[d], k0[d], 0x108, 0xf, 0x3, false);
-                    }
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int r = c * kChunk + 16 * t + 8 * h + (m16 & 7);
-                        const int n = (r >= An) ? -1 : (DENSE && active_idx == nullptr) ? r : aidx_s[r];
-                        const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
-                        __builtin_amdgcn_raw_buffer_store_b128(rows[h], rk, off + 16 * kpiece, 0, kNT);
-                    }
-                }
+                const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(kc_u, N * kD * 2);
+                const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vc_u, N * kD * 2);
+                // K and V are held as whole rows (see issue): every store
+                // writes 8 complete 128-byte rows; K row 8k + m16 % 8 is in
+                // k[k / 2][k % 2], V's in v[k].
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const int r = c * kChunk + 8 * k + (lane >> 3);
+                    const int r = c * kChunk + 8 * k + (m16 & 7);
                     const int n = (r >= An) ? -1 : (DENSE && active_idx == nullptr) ? r : aidx_s[r];
-                    const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) : kSkip;
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.v[k]),
-                                                           rv, off + 16 * (lane & 7), 0, kNT);
+                    const uint32_t off =
+                        (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) + 16 * kpiece : kSkip;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4_t, ch.k[k >> 1][k & 1]), rk, off, 0, kNT);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, ch.v[k]), rv,
+                                                           off, 0, kNT);
                 }
             }
         }
@@ -552,6 +584,11 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
             const uint2 hi = lds_tr_b64(tile + vofs[1][dt]);
             va[dt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
+        // K rows into the operand layout: kop[t][0] = piece g, kop[t][1] =
+        // piece 4 + g of key row 16t + m16.
+        uint4 kop[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) swap_row_halves(ch.k[t][0], ch.k[t][1], kop[t][0], kop[t][1]);
         // wave-uniform
         const bool full = DENSE ? (c * kChunk + kChunk <= An) : ch.valid == 0xffffffffu;
 #pragma unroll
@@ -562,9 +599,9 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ch.k[t][0]), qf[qt][0],
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[t][0]), qf[qt][0],
                                                               acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ch.k[t][1]), qf[qt][1],
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[t][1]), qf[qt][1],
                                                               acc, 0, 0, 0);
                 s[t] = acc;
             }
@@ -778,6 +815,10 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     static_assert(!RAGGED || (CACHED && !UPDATE), "per-sequence counts: cached rows, no update");
     constexpr int kQ = 16 * NQT;         // queries per wave
     constexpr int kPasses = 4 / W;       // load passes per chunk (8 W rows each)
+    // The chunk loads (whole rows, 8 lanes per row): streaming with cached
+    // rows; plain without them (the full-attention layers, where the
+    // workgroups of a longer unit share its chunks through L2).
+    constexpr int kWgLoadPolicy = CACHED ? kStreamPolicy : 0;
     __shared__ __align__(16) unsigned char lds[4 * kWgTile];  // 2 buffers x (K tile, V tile)
     static_assert(4 * kWgTile >= W * 2048, "the output staging reuses the K/V tiles");
     // CACHED: the staged lists after the tiles, [max(Nc, 1)] entries, the
@@ -817,10 +858,8 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     const int A0 = CACHED ? na * kChunk : A;
     const int T = CACHED ? A0 + Ncn : A;  // rows of the unit's (padded) sequence
     const int nchunks = (T + kChunk - 1) / kChunk;
-    const __amdgpu_buffer_rsrc_t rka = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(k_a + ub), 0, A * kD * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rva = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(v_a + ub), 0, A * kD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rka = uniform_rsrc(k_a + ub, A * kD * 2);
+    const __amdgpu_buffer_rsrc_t rva = uniform_rsrc(v_a + ub, A * kD * 2);
     const size_t cb = static_cast<size_t>(u) * N * kD;  // the unit's cache rows (CACHED)
 
     int32_t* cidx_s = wg_lists;                       // [max(Nc, 1)]
@@ -831,14 +870,12 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     // buffer reads as zero).  A row past A (no cached rows), a skipped cached
     // entry or a row past the sequence reads as zero and is masked.
     const int lrow = tid >> 3;
-    const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(k_cache + (CACHED ? cb : 0)), 0, CACHED ? N * kD * 2 : 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(v_cache + (CACHED ? cb : 0)), 0, CACHED ? N * kD * 2 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rkc = uniform_rsrc(k_cache + (CACHED ? cb : 0), CACHED ? N * kD * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rvc = uniform_rsrc(v_cache + (CACHED ? cb : 0), CACHED ? N * kD * 2 : 0);
     auto load = [&](int c, uint4 (&kk)[kPasses], uint4 (&vv)[kPasses]) __attribute__((always_inline)) {
         constexpr uint32_t kOut = 0x80000000u;  // past any buffer: reads as zero
         auto ld = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t ofs) __attribute__((always_inline)) {
-            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, ofs, 0, 0));
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, ofs, 0, kWgLoadPolicy));
         };
         const int r0 = c * kChunk;
         const uint32_t piece = 16 * (tid & 7);
@@ -875,9 +912,9 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
             constexpr int kNT = 2;  // nontemporal (streaming) store
             const int rows = CACHED ? N : A;
             const __amdgpu_buffer_rsrc_t rk =
-                __builtin_amdgcn_make_buffer_rsrc(k_cache + (CACHED ? cb : ub), 0, rows * kD * 2, 0x00020000);
+                uniform_rsrc(k_cache + (CACHED ? cb : ub), rows * kD * 2);
             const __amdgpu_buffer_rsrc_t rv =
-                __builtin_amdgcn_make_buffer_rsrc(v_cache + (CACHED ? cb : ub), 0, rows * kD * 2, 0x00020000);
+                uniform_rsrc(v_cache + (CACHED ? cb : ub), rows * kD * 2);
             if (CACHED ? (c * kChunk < A) : (c < nchunks && c % n_blocks == qb)) {  // uniform
 #pragma unroll
                 for (int p = 0; p < kPasses; ++p) {
