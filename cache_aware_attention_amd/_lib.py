@@ -95,6 +95,53 @@ def _check(fn: str, status: int):
         raise MarError(fn, status, load_library().mar_status_string(status).decode())
 
 
+_capture = None  # a list while prepare() records calls
+
+
+def _call(name: str, *args):
+    """Call a device entry point with marshalled arguments (or record the call
+    when prepare() is capturing) and raise MarError on a negative status."""
+    fn = getattr(load_library(), name)
+    if _capture is not None:
+        _capture.append((name, fn, args))
+        return
+    _check(name, fn(*args))
+
+
+class Prepared:
+    """Library calls whose arguments were checked and marshalled once: calling
+    the object makes the same C calls again (same device pointers, sizes and
+    stream), paying only for the foreign calls themselves."""
+
+    def __init__(self, calls):
+        self.calls = calls
+
+    def __call__(self):
+        for name, fn, args in self.calls:
+            st = fn(*args)
+            if st != MAR_OK:
+                _check(name, st)
+
+
+def prepare(fn, *args, **kwargs) -> Prepared:
+    """Run the binding function fn(*args, **kwargs) once without executing its
+    library calls: its checks and argument marshalling happen now (including
+    the choice of stream, the current one unless given), and the returned
+    Prepared replays the calls.  Every tensor it refers to must stay alive and
+    in place while the Prepared is used; outputs fn would allocate are
+    allocated once, here."""
+    global _capture
+    if _capture is not None:
+        raise RuntimeError("prepare() does not nest")
+    _capture = []
+    try:
+        fn(*args, **kwargs)
+        calls = _capture
+    finally:
+        _capture = None
+    return Prepared(calls)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return MAR_F32
@@ -150,12 +197,11 @@ def mar_cache_attn_fwd(q_a, k_a, v_a, k_cache, v_cache, cached_idx, Nc=None, out
         _dev(lse, "lse", torch.float32, (B, H, A))
     if scale is None:
         scale = D ** -0.5
-    st = load_library().mar_cache_attn_fwd(
+    _call("mar_cache_attn_fwd",
         _dev(q_a, "q_a"), _dev(k_a, "k_a"), _dev(v_a, "v_a"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), cptr, ldc, _dev(out, "out"),
         _dev(lse, "lse") if lse is not None else None, B, H, N, A, Nc, D, float(scale), code,
         _stream(stream))
-    _check("mar_cache_attn_fwd", st)
     return out
 
 
@@ -188,12 +234,11 @@ def mar_cache_attn_fwd_ragged(q_a, k_a, v_a, k_cache, v_cache, cached_idx, a_len
         _dev(lse, "lse", torch.float32, (B, H, A))
     if scale is None:
         scale = D ** -0.5
-    st = load_library().mar_cache_attn_fwd_ragged(
+    _call("mar_cache_attn_fwd_ragged",
         _dev(q_a, "q_a"), _dev(k_a, "k_a"), _dev(v_a, "v_a"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), cptr, ldc, _dev(a_len, "a_len"), _dev(c_len, "c_len"),
         _dev(out, "out"), _dev(lse, "lse") if lse is not None else None, B, H, N, A, ldc, D,
         float(scale), code, _stream(stream))
-    _check("mar_cache_attn_fwd_ragged", st)
     return out
 
 
@@ -237,13 +282,12 @@ def mar_cache_attn_fwd_update(q_a, k_a, v_a, k_cache, v_cache, cached_idx, activ
         _dev(err_count, "err_count", torch.int32)
     if scale is None:
         scale = D ** -0.5
-    st = load_library().mar_cache_attn_fwd_update(
+    _call("mar_cache_attn_fwd_update",
         _dev(q_a, "q_a"), _dev(k_a, "k_a"), _dev(v_a, "v_a"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), cptr, ldc, aptr, ld_act,
         _dev(err_count, "err_count") if err_count is not None else None, _dev(out, "out"),
         _dev(lse, "lse") if lse is not None else None, B, H, N, A, Nc, D, float(scale), code,
         _stream(stream))
-    _check("mar_cache_attn_fwd_update", st)
     return out
 
 
@@ -261,11 +305,10 @@ def mar_kv_scatter_refresh(k_cache, v_cache, k_new, v_new, idx=None, err_count=N
         if idx.dim() != 2 or idx.shape[0] != B:
             raise ValueError("idx must be [B, ld_idx]")
         ld = idx.shape[1]
-    st = load_library().mar_kv_scatter_refresh(
+    _call("mar_kv_scatter_refresh",
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_new, "k_new"),
         _dev(v_new, "v_new"), _dev(idx, "idx", torch.int32), ld,
         _dev(err_count, "err_count", torch.int32), B, H, N, M, D, code, _stream(stream))
-    _check("mar_kv_scatter_refresh", st)
 
 
 def mar_refresh_topk_workspace(B: int, H: int, N: int) -> int:
@@ -310,22 +353,20 @@ def mar_refresh_topk(q_gen, k_full, gp_idx, n_gp, K, scores=None, active_idx=Non
             raise ValueError("gp_idx must be a GPU int32 tensor")
         gp_ptr = ctypes.c_void_p(gp_idx.data_ptr())
     if _noalloc:
-        st = load_library().mar_refresh_topk_noalloc(
+        _call("mar_refresh_topk_noalloc",
             _dev(q_gen, "q_gen"), _dev(k_full, "k_full"), gp_ptr, ld_gp, int(n_gp), int(K),
             float(D ** -0.5 if scale is None else scale), _dev(scores, "scores"),
             _dev(active_idx, "active_idx", torch.int32), active_idx.shape[1],
             _dev(cached_idx, "cached_idx", torch.int32), cached_idx.shape[1],
             _dev(cached_len, "cached_len"), B, H, G, N, D, code, _stream(stream))
-        _check("mar_refresh_topk_noalloc", st)
         return scores, active_idx, cached_idx, cached_len
-    st = load_library().mar_refresh_topk(
+    _call("mar_refresh_topk",
         _dev(q_gen, "q_gen"), _dev(k_full, "k_full"), gp_ptr, ld_gp, int(n_gp), int(K),
         float(D ** -0.5 if scale is None else scale), _dev(scores, "scores"),
         _dev(active_idx, "active_idx", torch.int32), active_idx.shape[1],
         _dev(cached_idx, "cached_idx", torch.int32), cached_idx.shape[1],
         _dev(cached_len, "cached_len"), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), B, H, G, N, D, code, _stream(stream))
-    _check("mar_refresh_topk", st)
     return scores, active_idx, cached_idx, cached_len
 
 
@@ -353,13 +394,12 @@ def mar_cos_gate(x_cur, x_cached, tau=0.95, eps=1e-8, cos_out=None, reuse_mask=N
         compute_idx = torch.empty((B, N), dtype=torch.int32, device=dev)
     if compute_len is None:
         compute_len = torch.empty((B,), dtype=torch.int32, device=dev)
-    st = load_library().mar_cos_gate(
+    _call("mar_cos_gate",
         _dev(x_cur, "x_cur"), _dev(x_cached, "x_cached"), float(tau), float(eps),
         _dev(cos_out, "cos_out", torch.float32, (B, N)),
         _dev(reuse_mask, "reuse_mask", torch.uint8, (B, N)),
         _dev(compute_idx, "compute_idx", torch.int32, (B, N)),
         _dev(compute_len, "compute_len", torch.int32, (B,)), B, N, W, code, _stream(stream))
-    _check("mar_cos_gate", st)
     return cos_out, reuse_mask, compute_idx, compute_len
 
 
@@ -380,12 +420,11 @@ def mar_cfg_residual(cond, uncond=None, residual=None, mode=MAR_CFG_STORE, uncon
     _dev(residual, "residual", f32, cond.shape)
     if guided_out is not None:
         _dev(guided_out, "guided_out", f32, cond.shape)
-    st = load_library().mar_cfg_residual(
+    _call("mar_cfg_residual",
         _dev(cond, "cond"), _dev(uncond, "uncond") if uncond is not None else None,
         _dev(residual, "residual"), _dev(uncond_out, "uncond_out") if uncond_out is not None else None,
         _dev(guided_out, "guided_out") if guided_out is not None else None, float(cfg_scale),
         int(mode), n, _stream(stream))
-    _check("mar_cfg_residual", st)
     return (residual if mode == MAR_CFG_STORE else uncond_out), guided_out
 
 

@@ -3,7 +3,7 @@
 // "LazyMAR" paper-notes page, Key designs (token cache): past the first three
 // layers, a token whose current feature is cosine-similar to the feature it
 // had when its cached value was computed skips recomputation.  Kernel 1
-// computes one cosine per token (16-byte loads, float accumulation of <x,y>,
+// computes one cosine per token (16-byte streaming loads, float accumulation of <x,y>,
 // |x|^2, |y|^2 per lane, then a wave reduction) and the reuse decision
 // cos >= tau in float: several tokens per wave with all their loads in
 // flight for widths up to 256 pieces of 16 bytes, one token per wave above.
@@ -51,11 +51,12 @@ __global__ __launch_bounds__(kThreads) void cosine_kernel(const V* __restrict__ 
     float xy = 0.f, xx = 0.f, yy = 0.f;
     int p = lane;
     for (; p + kWave < pieces; p += 2 * kWave) {
-        const V a0 = xr[p], c0 = yr[p], a1 = xr[p + kWave], c1 = yr[p + kWave];
+        const V a0 = ld_stream(xr + p), c0 = ld_stream(yr + p), a1 = ld_stream(xr + p + kWave),
+                c1 = ld_stream(yr + p + kWave);
         acc_piece(a0, c0, xy, xx, yy);
         acc_piece(a1, c1, xy, xx, yy);
     }
-    if (p < pieces) acc_piece(xr[p], yr[p], xy, xx, yy);
+    if (p < pieces) acc_piece(ld_stream(xr + p), ld_stream(yr + p), xy, xx, yy);
     xy = wave_sum(xy);
     xx = wave_sum(xx);
     yy = wave_sum(yy);
@@ -90,8 +91,8 @@ __global__ __launch_bounds__(kThreads) void cosine_multi_kernel(
         for (int i = 0; i < kPPL; ++i) {
             const int p = lane + kWave * i;
             const int pc = (p < pieces) ? p : 0;  // lanes past the row reload piece 0 (unused)
-            xa[k][i] = xr[pc];
-            ya[k][i] = yr[pc];
+            xa[k][i] = ld_stream(xr + pc);
+            ya[k][i] = ld_stream(yr + pc);
         }
     }
     float xy[kTPW], xx[kTPW], yy[kTPW];

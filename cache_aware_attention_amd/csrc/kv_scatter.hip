@@ -6,7 +6,7 @@
 // Full refresh: on every third step the whole cache is rewritten ("MARche"
 // paper-notes page, Key Design 3 and flowchart).
 //
-// Both are pure data movement: 16-byte vector loads/stores, every byte of
+// Both are pure data movement: 16-byte streaming loads/stores, every byte of
 // the source read once and every destination byte written once.  The partial
 // kernel assigns one thread per 16-byte piece of a (b, m, h) row pair, so a
 // wave covers whole 128-byte rows (bf16, D = 64) and stays coalesced.
@@ -15,8 +15,6 @@
 
 namespace marca {
 namespace {
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // Threads = B * M * H * pieces (pieces = row_bytes / 16), K and V in the same
 // thread.  Index order: piece fastest, then h, then m, then b.
@@ -41,38 +39,43 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
     const size_t dst = (((size_t)b * H + h) * N + j) * pieces + piece;
     // Nontemporal stores: the rows are read again only at a later step, and
     // streaming them out now keeps their write-back out of the next kernel.
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, k_new[src]),
-                                reinterpret_cast<u32x4_t*>(k_cache + dst));
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v_new[src]),
-                                reinterpret_cast<u32x4_t*>(v_cache + dst));
+    st_stream(k_cache + dst, ld_stream(k_new + src));
+    st_stream(v_cache + dst, ld_stream(v_new + src));
 }
 
-// Full rewrite: grid-stride copy of n16 16-byte pieces of both tensors, four
-// pieces in flight per thread per iteration.
+// Full rewrite: each wave copies contiguous groups of 4 KB of both tensors
+// (four 1 KB pieces in flight per tensor), grid-stride over the groups, with
+// streaming loads and stores (whole lines, read and written once); the tail
+// below one group goes piece by piece.
+constexpr int kCopyUnroll = 4;
 __global__ __launch_bounds__(256) void copy_full_kernel(uint4* __restrict__ k_cache,
                                                         uint4* __restrict__ v_cache,
                                                         const uint4* __restrict__ k_new,
                                                         const uint4* __restrict__ v_new,
                                                         long long n16) {
-    const long long stride = (long long)gridDim.x * blockDim.x;
-    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 k0 = k_new[i], k1 = k_new[i + stride], k2 = k_new[i + 2 * stride],
-                    k3 = k_new[i + 3 * stride];
-        const uint4 v0 = v_new[i], v1 = v_new[i + stride], v2 = v_new[i + 2 * stride],
-                    v3 = v_new[i + 3 * stride];
-        k_cache[i] = k0;
-        k_cache[i + stride] = k1;
-        k_cache[i + 2 * stride] = k2;
-        k_cache[i + 3 * stride] = k3;
-        v_cache[i] = v0;
-        v_cache[i + stride] = v1;
-        v_cache[i + 2 * stride] = v2;
-        v_cache[i + 3 * stride] = v3;
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    const long long n_waves = (long long)gridDim.x * blockDim.x / kWave;
+    constexpr long long kGroup = kCopyUnroll * kWave;  // pieces per group
+    const long long n_groups = n16 / kGroup;
+    for (long long gi = wave; gi < n_groups; gi += n_waves) {
+        const long long base = gi * kGroup + lane;
+        uint4 k[kCopyUnroll], v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            k[u] = ld_stream(k_new + base + u * kWave);
+            v[u] = ld_stream(v_new + base + u * kWave);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            st_stream(k_cache + base + u * kWave, k[u]);
+            st_stream(v_cache + base + u * kWave, v[u]);
+        }
     }
-    for (; i < n16; i += stride) {
-        k_cache[i] = k_new[i];
-        v_cache[i] = v_new[i];
+    const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    for (long long i = n_groups * kGroup + tid; i < n16; i += (long long)gridDim.x * blockDim.x) {
+        st_stream(k_cache + i, ld_stream(k_new + i));
+        st_stream(v_cache + i, ld_stream(v_new + i));
     }
 }
 
@@ -89,9 +92,9 @@ int launch_kv_scatter(void* k_cache, void* v_cache, const void* k_new, const voi
     const uint4* vn = static_cast<const uint4*>(v_new);
     if (idx == nullptr) {
         const long long n16 = (long long)B * H * N * pieces;
-        // ~8 waves per CU of 256 CUs, each thread moving 4 pieces per pass
-        long long blocks = (n16 + 256 * 4 - 1) / (256 * 4);
-        if (blocks > 2048) blocks = 2048;
+        // two waves per SIMD (512 workgroups of 4 waves), fewer for small copies
+        long long blocks = (n16 + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll);
+        if (blocks > 512) blocks = 512;
         if (blocks < 1) blocks = 1;
         hipLaunchKernelGGL(copy_full_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, kc, vc,
                            kn, vn, n16);

@@ -346,16 +346,23 @@ __global__ __launch_bounds__(64 * W) void refresh_scores_reg_kernel(
     const bf16x8_t qa1 = __builtin_bit_cast(bf16x8_t, qhi);
     const uint16_t* K = k_full + (size_t)u * N * kD;
 
-    // Every tile's key rows are requested before the first MFMA; a key past
-    // N (partial or missing tile) reads row 0 and is masked below.
+    // Every tile's key rows are requested before the first MFMA, as whole
+    // 128-byte rows with streaming loads (lane: piece kpiece of key
+    // 16 (w + W k) + 8h + m16 % 8), then exchanged into the operand layout
+    // (piece g and 4 + g of key 16 (w + W k) + m16); a key past N (partial
+    // or missing tile) reads row 0 and is masked below.
+    const int kpiece = (m16 < 8) ? g : 4 + g;
     uint4 kr[TPW][2];
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-        const int key = 16 * (w + W * k) + m16;
-        const uint4* p = reinterpret_cast<const uint4*>(K + (size_t)(key < N ? key : 0) * kD);
-        kr[k][0] = p[g];
-        kr[k][1] = p[4 + g];
-    }
+    for (int k = 0; k < TPW; ++k)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key = 16 * (w + W * k) + 8 * h + (m16 & 7);
+            kr[k][h] = ld_stream(reinterpret_cast<const uint4*>(K + (size_t)(key < N ? key : 0) * kD) +
+                                 kpiece);
+        }
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) swap_row_halves(kr[k][0], kr[k][1], kr[k][0], kr[k][1]);
     // s[k][i] = scale_log2 * S[query 4g+i][key 16 (w + W k) + m16]
     f32x4_t s[TPW];
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};

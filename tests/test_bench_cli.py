@@ -79,3 +79,22 @@ def test_headline_record_contract():
     assert r["frac"] == 5400.0 / 8000.0 and r["traffic"] == 1.9e8
     assert rec["cpu_baseline"] is cpu
     json.dumps(rec)  # serialisable as one line
+
+
+def test_full_attention_roofline_bound():
+    """The full-attention layer's roofline is chosen by its intensity against the
+    bf16 ridge (2500 TFLOP/s over 8 TB/s = 312.5 flop/B): MAR-L's 320-token layer
+    (4 B H N^2 D flops over 4 B H N D bf16 bytes = N/2 = 160 flop/B) is HBM-bound,
+    the high-res 1088-token layer (544 flop/B) matrix-core-bound."""
+    b = load_bench()
+    assert b.RIDGE_FLOP_PER_BYTE == 312.5
+    B, H, N, D = 128, 16, 320, 64
+    flops, nbytes = 4 * B * H * N * N * D, 4 * B * H * N * D * 2
+    r = b.roofline_for(flops, nbytes, 77.0e-6)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["flop_per_byte"] == 160.0
+    assert abs(r["achieved"] - nbytes / 77.0e-6 / 1e9) < 1e-6 and r["frac"] == r["achieved"] / 8000.0
+    B, N = 64, 1088
+    flops, nbytes = 4 * B * H * N * N * D, 4 * B * H * N * D * 2
+    r = b.roofline_for(flops, nbytes, 356.0e-6)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["flop_per_byte"] == 544.0
+    assert r["frac"] == r["achieved"] / 2500.0
