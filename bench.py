@@ -243,6 +243,95 @@ def seq_view(x, nb):
     return v
 
 
+def time_rotating(fn, items, stream, R=5, warm_s=0.05):
+    """Per-call time of fn over the rotating items: a warm-up of at least
+    warm_s seconds, then HIP events on `stream` around R passes."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for it in items:
+            fn(it)
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(R):
+        for it in items:
+            fn(it)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (R * len(items))
+
+
+LOCALITY_SPLITS = (48, 128)  # active tokens of 320; the rest are cached
+LOCALITY_LAYERS = 8
+
+
+def locality_inputs(marca, dev, A, stream):
+    """LOCALITY_LAYERS distinct MAR-L layer-calls with A active of 320 tokens,
+    each with prepared calls of: the cache-aware attention (cached rows
+    gathered through the list), the concatenation [active ; cached] of
+    standard attention, and the same attention kernel over the concatenated
+    rows (the list then names contiguous rows A .. 319 of the concatenation)."""
+    import torch
+
+    from cache_aware_attention_amd import _bench_lib
+    from mar_workloads import CONFIGS, attention_inputs
+    cfg = CONFIGS["mar_l"]
+    Nc = cfg.N - A
+    layers = []
+    for l in range(LOCALITY_LAYERS):
+        x = attention_inputs(cfg, dev, seed=cfg.seed * 100 + 70 + l, A=A)
+        x["out"] = torch.empty_like(x["q_a"])
+        x["kcat"] = torch.empty_like(x["k_cache"])
+        x["vcat"] = torch.empty_like(x["v_cache"])
+        x["contig"] = (torch.arange(A, cfg.N, dtype=torch.int32, device=dev)
+                       .expand(cfg.B, Nc).contiguous())
+        x["p_ca"] = marca.prepare(marca.mar_cache_attn_fwd, x["q_a"], x["k_a"], x["v_a"],
+                                  x["k_cache"], x["v_cache"], x["cached"], Nc=Nc, out=x["out"],
+                                  stream=stream)
+        x["p_cat"] = marca.prepare(_bench_lib.mar_bench_kv_concat, x["k_a"], x["v_a"],
+                                   x["k_cache"], x["v_cache"], x["cached"], Nc, x["kcat"],
+                                   x["vcat"], stream=stream)
+        x["p_std"] = marca.prepare(marca.mar_cache_attn_fwd, x["q_a"], x["k_a"], x["v_a"],
+                                   x["kcat"], x["vcat"], x["contig"], Nc=Nc, out=x["out"],
+                                   stream=stream)
+        layers.append(x)
+    torch.cuda.synchronize()
+    return cfg, layers
+
+
+def locality(marca, dev, stream):
+    """The pages' comparison of standard attention (physically concatenating
+    the cached and the fresh K/V, then attending) with cache-aware attention
+    (no concatenation), at equal work: one MAR-L layer-call (128 sequences x
+    16 heads, 320 tokens) with A = 48 and A = 128 active tokens.  Reports the
+    cache-aware call, the concatenation, and the same attention kernel over
+    the concatenated (contiguous) rows; standard = concatenation + attention.
+    Also the same attention with only the cached rows' order changed, which
+    is what memory locality alone is worth to the attention."""
+    import torch
+    res = []
+    for A in LOCALITY_SPLITS:
+        cfg, layers = locality_inputs(marca, dev, A, stream)
+        Nc = cfg.N - A
+        for x in layers:
+            x["p_cat"]()  # the concatenations exist before the contiguous attention runs
+        t_ca = time_rotating(lambda x: x["p_ca"](), layers, stream)
+        t_cat = time_rotating(lambda x: x["p_cat"](), layers, stream)
+        t_contig = time_rotating(lambda x: x["p_std"](), layers, stream)
+        res.append({"active": A, "cached": Nc, "cache_aware_us": t_ca, "concat_us": t_cat,
+                    "attention_on_concat_us": t_contig, "standard_us": t_cat + t_contig,
+                    "standard_over_cache_aware": (t_cat + t_contig) / t_ca,
+                    "contiguous_over_gathered": t_contig / t_ca,
+                    "concat_bytes": 2 * 2 * cfg.B * cfg.H * (A + Nc) * cfg.D * 2 + cfg.B * Nc * 4})
+        del layers
+        torch.cuda.empty_cache()
+    return {"what": "standard attention (concatenate [active ; cached] K/V, then attend) vs "
+                    "cache-aware attention, one MAR-L layer-call per split",
+            "splits": res}
+
+
 def other_configs(marca, dev, stream):
     """The cache-aware attention call (and, at the high-res length, the full
     attention and refresh-step calls) at the other configurations' shapes:
@@ -328,6 +417,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the whole-decode timing (for counter runs)")
+    ap.add_argument("--locality-only", action="store_true",
+                    help="only the locality comparison's kernels, a fixed sequence (counter runs)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the plain copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -345,6 +436,26 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = CONFIGS["mar_l"]
+
+    if args.locality_only:
+        # Per split, in this order: 3 passes of the cache-aware attention over
+        # its layers, then 3 of the concatenation, then 3 of the attention over
+        # the concatenated rows; one line of JSON with the dispatch order.
+        stream = torch.cuda.current_stream()
+        order = []
+        for A in LOCALITY_SPLITS:
+            _, layers = locality_inputs(marca, dev, A, stream)
+            for key, name in (("p_ca", "cache_aware"), ("p_cat", "concat"),
+                              ("p_std", "attention_on_concat")):
+                for _ in range(3):
+                    for x in layers:
+                        x[key]()
+                order.append({"active": A, "variant": name, "launches": 3 * len(layers)})
+            torch.cuda.synchronize()
+            del layers
+            torch.cuda.empty_cache()
+        print(json.dumps({"dispatch_order": order}))
+        return
 
     if args.copy_only:
         # plain copy of a known size through the full-refresh kernel: 2 x 256 MiB read,
@@ -528,6 +639,17 @@ def main():
 
     plans = [marca.mar_plan_step(decode_counts, t, cfg.N, cfg.budget) for t in range(cfg.steps)]
 
+    from cache_aware_attention_amd import _bench_lib
+
+    def pattern(l, write_out):
+        """The attention's memory operations without its arithmetic (its
+        access-pattern floor), on layer l's buffers."""
+        x = X[0]
+        L = x["layers"][l]
+        prepared(("pattern", l, write_out), _bench_lib.mar_bench_attn_pattern, L["q_a"], L["k_a"],
+                 L["v_a"], L["k_cache"], L["v_cache"], x["cached_idx"], cfg.Nc, L["out"],
+                 write_out=write_out, stream=stream)()
+
     def timed_kernels():
         """The same launches as one step, grouped by kernel so that one pair of HIP
         events brackets each group of back-to-back launches (an event pair around
@@ -547,6 +669,8 @@ def main():
         span("gate", gate, 1)
         span("full_attn", lambda: [full_attn(l) for l in range(n_ca)], n_ca)
         span("full_refresh", lambda: [full_refresh(l) for l in range(n_ca)], n_ca)
+        span("attn_pattern", lambda: [pattern(l, True) for l in range(n_ca)], n_ca)
+        span("attn_pattern_reads", lambda: [pattern(l, False) for l in range(n_ca)], n_ca)
         return spans
 
     print("bench: warmup", file=sys.stderr, flush=True)
@@ -652,6 +776,7 @@ def main():
         print(f"bench: copy measurement failed: {exc}", file=sys.stderr)
 
     configs = None if args.no_decode else other_configs(marca, dev, stream)
+    loc = None if args.no_decode else locality(marca, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -694,6 +819,13 @@ def main():
             "ms_cond_cache": decode_ms.get("cache+cond"),
             "speedup_cond_cache": decode_ms.get("none", 0) / decode_ms.get("cache+cond", 1)},
         "configs": configs,
+        "attn_pattern": {
+            "what": "the attention's memory operations without its arithmetic "
+                    "(mar_bench_attn_pattern): the floor of its access pattern, same buffers",
+            "us_per_call": avg_us["attn_pattern"],
+            "reads_only_us_per_call": avg_us["attn_pattern_reads"],
+            "attn_over_pattern": avg_us["attn"] / avg_us["attn_pattern"]},
+        "locality": loc,
         "attn_median_us": attn_median_us,
         "attn_frac_of_copy": (achieved / copy_gbs) if copy_gbs else None,
         "attn_bytes_per_call": bytes_call,

@@ -98,10 +98,10 @@ def _check(fn: str, status: int):
 _capture = None  # a list while prepare() records calls
 
 
-def _call(name: str, *args):
+def _call(name: str, *args, lib=None):
     """Call a device entry point with marshalled arguments (or record the call
     when prepare() is capturing) and raise MarError on a negative status."""
-    fn = getattr(load_library(), name)
+    fn = getattr(lib if lib is not None else load_library(), name)
     if _capture is not None:
         _capture.append((name, fn, args))
         return

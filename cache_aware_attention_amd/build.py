@@ -21,6 +21,10 @@ LIB = PKG / "libmarca.so"
 
 HIP_SOURCES = ["cache_attn.hip", "kv_scatter.hip", "refresh_topk.hip", "cos_gate.hip",
                "cfg_residual.hip"]
+# Measurement kernels (include/mar_bench.h), a library of their own: the
+# decoding path never loads it.
+BENCH_SOURCES = ["bench_kernels.hip"]
+BENCH_LIB = PKG / "libmarca_bench.so"
 CPP_SOURCES = ["abi.cpp", "schedule.cpp"]
 # Per-file device flags.  The attention kernels assume NaN-free inputs (a
 # documented precondition of the ABI), which lets the compiler take maxima of
@@ -57,7 +61,7 @@ def _run(cmd):
 def build(verbose: bool = False) -> Path:
     BUILD.mkdir(exist_ok=True)
     jobs = []
-    for src in HIP_SOURCES:
+    for src in HIP_SOURCES + BENCH_SOURCES:
         obj = BUILD / (src + ".o")
         jobs.append([hipcc(), *hip_flags(), *HIP_EXTRA_FLAGS.get(src, []), "-c", str(CSRC / src),
                      "-o", str(obj)])
@@ -67,12 +71,13 @@ def build(verbose: bool = False) -> Path:
                      f"-I{INCLUDE}", f"-I{CSRC}", "-c", str(CSRC / src), "-o", str(obj)])
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
         list(ex.map(_run, jobs))
-    objs = [str(BUILD / (s + ".o")) for s in HIP_SOURCES + CPP_SOURCES]
-    tmp = LIB.with_suffix(f".so.tmp{os.getpid()}")
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *objs])
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+    for lib, sources in ((LIB, HIP_SOURCES + CPP_SOURCES), (BENCH_LIB, BENCH_SOURCES)):
+        objs = [str(BUILD / (s + ".o")) for s in sources]
+        tmp = lib.with_suffix(f".so.tmp{os.getpid()}")
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *objs])
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib}")
     return LIB
 
 

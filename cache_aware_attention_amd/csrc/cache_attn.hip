@@ -369,8 +369,12 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         qf[qt][1] = as_bf16x8(y);
     }
 
+    // A chunk at or past the wave's range end (requested only to keep every
+    // step's loads alike) is made of rows past the sequence: missing rows,
+    // which read active row 0 (one line per load instruction) or, in the
+    // dense form, past the buffer (zeros, no memory traffic).
     auto issue = [&](int c, ChunkRegs& cr) __attribute__((always_inline)) {
-        const int r0 = c * kChunk;
+        const int r0 = (c < ce ? c : nchunks) * kChunk;
         if constexpr (DENSE) {
             const int rb = r0 * (kD * 2);
 #pragma unroll
@@ -441,8 +445,8 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 
     // Chunk i (i < kPF) starts in cr[i].  A first chunk made only of active
     // rows does not need the cached list and is requested before it arrives.
-    // When the sequence has fewer than kPF chunks the spare buffers load its
-    // last chunk again (never used), so every path issues the same loads.
+    // When the sequence has fewer than kPF chunks the spare buffers load
+    // chunks past the end (never used), so every path issues the same loads.
     ChunkRegs cr[kPF + 1];
     if constexpr (SPLIT == 1) {
         if (An >= kChunk) {
@@ -453,20 +457,19 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
             issue(0, cr[0]);
         }
 #pragma unroll
-        for (int k = 1; k < kPF; ++k) issue(min(k, nchunks - 1), cr[k]);
+        for (int k = 1; k < kPF; ++k) issue(k, cr[k]);
     } else {
-        // A wave with no chunks (cb == ce) requests the unit's last chunk
+        // A wave with no chunks (cb == ce) requests a chunk past its range
         // and never computes it.
-        const int c0 = min(cb, nchunks - 1);
-        if ((c0 + 1) * kChunk <= An) {
-            issue(c0, cr[0]);
+        if ((cb + 1) * kChunk <= An) {
+            issue(cb, cr[0]);
             stage_list();
         } else {
             stage_list();
-            issue(c0, cr[0]);
+            issue(cb, cr[0]);
         }
 #pragma unroll
-        for (int k = 1; k < kPF; ++k) issue(max(min(cb + k, ce - 1), c0), cr[k]);
+        for (int k = 1; k < kPF; ++k) issue(cb + k, cr[k]);
     }
     // Per-lane LDS byte offsets of the V^T transposing reads: lane s of its
     // 16-lane group addresses key row 16h + 4g + s/4, head dims 16dt + 4(s%4).
@@ -597,16 +600,16 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 
     // Chunk c lives in cr[c % (kPF + 1)].  Each step requests chunk c + kPF
     // into the buffer chunk c - 1 just left, then computes chunk c.  Near the
-    // end the request is clamped to the last chunk, which was fetched a moment
-    // earlier and is served by L2: every step then issues the same loads, so
-    // the compiler's memory-counter waits stay exact with kPF chunks in flight
-    // (a conditional request would make them wait for everything).  The loop
-    // is unrolled by kPF + 1 so every register buffer index is a constant.
+    // end the request is for a chunk past the range (see issue: it reads one
+    // line per load, or nothing), so every step issues the same loads and the
+    // compiler's memory-counter waits stay exact with kPF chunks in flight (a
+    // conditional request would make them wait for everything).  The loop is
+    // unrolled by kPF + 1 so every register buffer index is a constant.
     auto step = [&](int c, auto buf_tag) __attribute__((always_inline)) {
         constexpr int BI = decltype(buf_tag)::value;
         constexpr int BN = (BI + kPF) % (kPF + 1);
         __builtin_amdgcn_s_setprio(3);  // requests first: they keep HBM busy
-        issue(min(c + kPF, ce - 1), cr[BN]);
+        issue(c + kPF, cr[BN]);
         __builtin_amdgcn_s_setprio(0);
         compute(c, cr[BI]);
     };
@@ -1059,8 +1062,8 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     // the staging registers, computes chunk c, stores chunk c + 1 into the
     // other buffer (whose chunk c - 1 every wave finished before the previous
     // barrier) and waits at the barrier.  Every step issues the same loads
-    // (past the end the last chunk is requested again and not used), so the
-    // compiler's memory-counter waits stay exact.
+    // (past the last chunk at out-of-range offsets, which read zeros without
+    // touching memory), so the compiler's memory-counter waits stay exact.
     uint4 sk[kPasses], sv[kPasses];
     load(0, sk, sv);  // chunk 0 holds active rows only (A > 64): no list needed
     if constexpr (CACHED) {
@@ -1115,7 +1118,7 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     __syncthreads();
     auto step = [&](int c, auto buf_tag, auto full_tag, auto first_tag, uint32_t rows = ~0u) __attribute__((always_inline)) {
         constexpr int BI = decltype(buf_tag)::value;
-        load(min(c + 1, nchunks - 1), sk, sv);
+        load(c + 1, sk, sv);  // past the last chunk: out-of-range offsets, no traffic
         if (nq > 0) compute(c, BI, rows, full_tag, first_tag);
         put(BI ^ 1, c + 1, sk, sv);
         __syncthreads();

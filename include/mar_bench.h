@@ -1,0 +1,58 @@
+/*
+ * mar_bench.h -- C ABI of libmarca_bench: measurement kernels that put the
+ * cache-aware attention of libmarca in context.  They are not part of the
+ * decoding path and the path never calls them.  Conventions (status codes,
+ * dtypes, layouts, caller-owned device buffers, asynchronous calls on
+ * `stream`) are those of mar_cache_attn.h.
+ */
+#ifndef MAR_BENCH_H
+#define MAR_BENCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mar_cache_attn.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * The memory operations of mar_cache_attn_fwd's one-wave kernel at A <= 64
+ * queries per (sequence, head) unit, without its arithmetic: the floor of
+ * that access pattern on this chip.  Reads q_a, k_a, v_a [B,H,A,D], the first
+ * Nc entries of each cached_idx row [B,ldc] and the cache rows they name in
+ * k_cache, v_cache [B,H,N,D], exactly as the attention does (entries outside
+ * [0,N) are not dereferenced).  write_out != 0: writes the A rows of each
+ * unit of out [B,H,A,D] with meaningless values, as many bytes as the
+ * attention's output; write_out == 0: reads only.
+ * Requires bf16 (MAR_E_UNSUPPORTED otherwise), D == 64, 1 <= A <= 64,
+ * A + Nc <= N, Nc <= 8192, ldc >= Nc.
+ */
+int mar_bench_attn_pattern(const void* q_a, const void* k_a, const void* v_a,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* cached_idx, int ldc, void* out, int write_out,
+                           int B, int H, int N, int A, int Nc, int D, int dtype, void* stream);
+
+/*
+ * The concatenation that standard attention performs before attending over
+ * the active and the cached tokens ([MARche] paper-notes page, Key Design 2;
+ * Pith review page, figure 7: standard versus cache-aware attention).  For
+ * T = A + Nc:
+ *   k_cat[b,h,r,:] = k_a[b,h,r,:]                         r < A
+ *   k_cat[b,h,r,:] = k_cache[b,h,cached_idx[b*ldc + r-A],:] A <= r < T
+ * and likewise for V.  k_cat, v_cat [B,H,T,D]; k_a, v_a [B,H,A,D];
+ * k_cache, v_cache [B,H,N,D].  An entry outside [0,N) leaves its row as it
+ * was.  Rows are copied bit for bit.  Requires D*sizeof(dtype) to be a
+ * multiple of 16 bytes, ldc >= Nc.
+ */
+int mar_bench_kv_concat(void* k_cat, void* v_cat, const void* k_a, const void* v_a,
+                        const void* k_cache, const void* v_cache,
+                        const int32_t* cached_idx, int ldc,
+                        int B, int H, int N, int A, int Nc, int D, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAR_BENCH_H */

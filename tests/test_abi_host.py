@@ -27,8 +27,8 @@ def lib():
     return _lib.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mar_[a-z0-9_]+)\s*\(", text)))
 
@@ -39,6 +39,31 @@ def test_exports_every_declared_function(lib):
     raw = ctypes.CDLL(str(_lib._LIB_PATH))
     for n in names:
         assert hasattr(raw, n), f"{n} not exported"
+
+
+def test_bench_library_exports_and_rejections():
+    """libmarca_bench (include/mar_bench.h, measurement kernels) exports what it
+    declares and refuses bad arguments before any GPU work."""
+    from cache_aware_attention_amd import _bench_lib
+    names = declared_functions(os.path.join(ROOT, "include", "mar_bench.h"))
+    assert names == ["mar_bench_attn_pattern", "mar_bench_kv_concat"]
+    b = _bench_lib.load_bench_library()
+    for n in names:
+        assert hasattr(ctypes.CDLL(str(_bench_lib._PATH)), n)
+    f = b.mar_bench_attn_pattern
+    # q, ka, va, kc, vc, cidx, ldc, out, write, B, H, N, A, Nc, D, dtype, stream
+    assert f(None, P, P, P, P, P, 272, P, 1, 2, 2, 320, 48, 272, 64, 1, None) == E_NULL
+    assert f(P, P, P, P, P, P, 272, P, 1, 2, 2, 320, 48, 272, 64, 0, None) == E_UNSUP   # fp32
+    assert f(P, P, P, P, P, P, 272, P, 1, 2, 2, 320, 49, 272, 64, 1, None) == E_SHAPE   # A+Nc > N
+    assert f(P, P, P, P, P, P, 272, P, 1, 2, 2, 400, 80, 272, 64, 1, None) == E_UNSUP   # A > 64
+    assert f(P, P, P, P, P, P, 100, P, 1, 2, 2, 320, 48, 272, 64, 1, None) == E_SHAPE   # ldc < Nc
+    assert f(P, P, P, P, P, P, 272, BAD, 1, 2, 2, 320, 48, 272, 64, 1, None) == E_RANGE
+    g = b.mar_bench_kv_concat
+    # kcat, vcat, ka, va, kc, vc, cidx, ldc, B, H, N, A, Nc, D, dtype, stream
+    assert g(None, P, P, P, P, P, P, 272, 2, 2, 320, 48, 272, 64, 1, None) == E_NULL
+    assert g(P, P, P, P, P, P, P, 272, 2, 2, 320, 48, 272, 64, 7, None) == E_DTYPE
+    assert g(P, P, P, P, P, P, P, 272, 2, 2, 320, 48, 272, 12, 1, None) == E_UNSUP    # 24-byte rows
+    assert g(P, P, P, P, P, P, P, 100, 2, 2, 320, 48, 272, 64, 1, None) == E_SHAPE
 
 
 def test_status_strings(lib):

@@ -1,0 +1,71 @@
+"""The measurement kernels of libmarca_bench on the GPU: the concatenation
+that standard attention needs is a bit-exact row copy (a skipped entry leaves
+its row as it was), and the attention's memory-operations-only kernel writes
+nothing outside its output rows (and nothing at all when told to only read)."""
+import numpy as np
+import pytest
+import torch
+
+from mar_workloads import CONFIGS, attention_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def bench():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import cache_aware_attention_amd  # noqa: F401  (loads libmarca first)
+    from cache_aware_attention_amd import _bench_lib
+    return _bench_lib
+
+
+def small(A, B=3, H=2):
+    cfg = CONFIGS["mar_l"].__class__(**{**CONFIGS["mar_l"].__dict__, "B": B, "H": H})
+    return attention_inputs(cfg, DEV, A=A), cfg
+
+
+@pytest.mark.parametrize("A", [48, 128])
+def test_concat_bit_exact(bench, A):
+    x, cfg = small(A)
+    Nc = cfg.N - A
+    cached = x["cached"].clone()
+    cached[1, 5] = -1       # a skipped entry: its row keeps the sentinel
+    cached[2, 0] = cfg.N    # out of range: skipped as well
+    kcat = torch.full((cfg.B, cfg.H, cfg.N, cfg.D), 7.0, dtype=torch.bfloat16, device=DEV)
+    vcat = kcat.clone()
+    bench.mar_bench_kv_concat(x["k_a"], x["v_a"], x["k_cache"], x["v_cache"], cached, Nc,
+                              kcat, vcat)
+    torch.cuda.synchronize()
+    i16 = lambda t: t.view(torch.int16).cpu().numpy()
+    ka, va, kc, vc = (i16(x[k]) for k in ("k_a", "v_a", "k_cache", "v_cache"))
+    cl = cached.cpu().numpy()
+    exp_k = np.full(i16(kcat).shape, i16(torch.tensor(7.0, dtype=torch.bfloat16)), np.int16)
+    exp_v = exp_k.copy()
+    exp_k[:, :, :A], exp_v[:, :, :A] = ka, va
+    for b in range(cfg.B):
+        for j in range(Nc):
+            n = cl[b, j]
+            if 0 <= n < cfg.N:
+                exp_k[b, :, A + j], exp_v[b, :, A + j] = kc[b, :, n], vc[b, :, n]
+    assert (i16(kcat) == exp_k).all() and (i16(vcat) == exp_v).all()
+
+
+def test_pattern_kernel_writes_only_its_rows(bench):
+    x, cfg = small(48)
+    B, H, A, D = x["q_a"].shape
+    sentinel = -12345
+    buf = torch.full((B * H * A * D + 4096,), sentinel, dtype=torch.int16, device=DEV)
+    out = buf[:B * H * A * D].view(torch.bfloat16).view(B, H, A, D)
+    bench.mar_bench_attn_pattern(x["q_a"], x["k_a"], x["v_a"], x["k_cache"], x["v_cache"],
+                                 x["cached"], cfg.Nc, out, write_out=False)
+    torch.cuda.synchronize()
+    assert (buf == sentinel).all()
+    bench.mar_bench_attn_pattern(x["q_a"], x["k_a"], x["v_a"], x["k_cache"], x["v_cache"],
+                                 x["cached"], cfg.Nc, out, write_out=True)
+    torch.cuda.synchronize()
+    assert (buf[B * H * A * D:] == sentinel).all()
+    # every 16-byte piece of the output rows was written
+    pieces = buf[:B * H * A * D].view(-1, 8)
+    assert not (pieces == sentinel).all(dim=1).any()
