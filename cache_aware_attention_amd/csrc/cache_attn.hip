@@ -184,6 +184,8 @@ constexpr int kChunk = 32;          // key rows per chunk (two 16-row MFMA tiles
 constexpr int kQueriesPerGroup = 64;
 constexpr int kMaxMfmaTokens = 8192;
 constexpr float kRescaleLog2 = 8.f;
+// LDS per one-wave workgroup that still fits 8 of them in a CU's 160 KB.
+constexpr size_t kStashLdsMax = 20 * 1024;
 // Chunks in flight ahead of the one computed: two where the registers allow
 // (up to 48 queries per wave), one for 64 queries.
 constexpr int prefetch_depth(int nqt) { return nqt <= 3 ? 2 : 1; }
@@ -261,7 +263,11 @@ struct ChunkRegs {
 // are rows 0..A-1 of k_a/v_a, read with range-checked buffer loads at
 // per-lane offsets fixed for the whole sequence.  A row past A reads as zero
 // and is masked like a missing row.
-template <int NQT, bool UPDATE, bool RAGGED, bool DENSE, int SPLIT = 1>
+// STASH (with UPDATE, one wave per unit): the active rows are copied to LDS as
+// they are read and written into the caches after the last chunk, beside the
+// output, instead of while the cached rows are being read (the cache writes
+// then no longer compete with the reads of every wave's first chunks).
+template <int NQT, bool UPDATE, bool RAGGED, bool DENSE, int SPLIT = 1, bool STASH = false>
 __global__ __launch_bounds__(64 * SPLIT) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
                       const uint16_t* __restrict__ v_a, const uint16_t* k_cache,
@@ -281,11 +287,14 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
     constexpr int kRegionBytes = (SPLIT / 2) * 64 * kState * 4 > SPLIT * kTileBytes
                                      ? (SPLIT / 2) * 64 * kState * 4
                                      : SPLIT * kTileBytes;
+    static_assert(!STASH || (UPDATE && !DENSE && SPLIT == 1), "stash: fused update, one wave");
     extern __shared__ __align__(16) unsigned char smem[];
     const int wv = (SPLIT > 1) ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
     unsigned char* tile = smem + wv * kTileBytes;  // V chunk, later the output tile
-    int32_t* cidx_s = reinterpret_cast<int32_t*>(smem + kRegionBytes);  // [max(Nc, 1)]
-    int32_t* aidx_s = cidx_s + (Nc > 0 ? Nc : 1);                       // [A] with UPDATE
+    unsigned char* stash = smem + kRegionBytes;    // STASH: [A] K rows, then [A] V rows
+    int32_t* cidx_s = reinterpret_cast<int32_t*>(smem + kRegionBytes +
+                                                 (STASH ? 2 * A * kD * 2 : 0));  // [max(Nc, 1)]
+    int32_t* aidx_s = cidx_s + (Nc > 0 ? Nc : 1);                                // [A] with UPDATE
 
     const int lane = (SPLIT > 1) ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
     const int g = lane >> 4;    // lane group: k-slot group of the MFMA operands
@@ -507,7 +516,18 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
             // unit's first query group (dense: every chunk holds active rows,
             // and the query groups take turns, chunk c written by group
             // c mod n_groups)
-            if (DENSE ? c % n_groups == qg : c * kChunk < An) {
+            if constexpr (STASH) {
+                if (c * kChunk < An) {  // wave-uniform: the chunk holds active rows
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int r = c * kChunk + 8 * k + (m16 & 7);
+                        if (r < An) {
+                            *reinterpret_cast<uint4*>(stash + swz(r, kpiece)) = ch.k[k >> 1][k & 1];
+                            *reinterpret_cast<uint4*>(stash + A * kD * 2 + swz(r, kpiece)) = ch.v[k];
+                        }
+                    }
+                }
+            } else if (DENSE ? c % n_groups == qg : c * kChunk < An) {
                 // Buffer stores: an offset past the unit's N rows (inactive
                 // lane, skipped entry) is dropped by the range check.
                 constexpr uint32_t kSkip = 0x80000000u;
@@ -678,6 +698,26 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
             __syncthreads();
         }
         if (wv != 0) return;  // after the last barrier
+    }
+
+    if constexpr (STASH) {
+        // The stashed active rows into the caches at their token positions:
+        // 8 whole rows per store, skipped entries dropped by the range check.
+        __syncthreads();  // one wave: orders the stash writes before the reads
+        constexpr uint32_t kSkip = 0x80000000u;
+        const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(kc_u, N * kD * 2);
+        const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vc_u, N * kD * 2);
+        for (int k = 0; k < (An + 7) / 8; ++k) {
+            const int r = 8 * k + (m16 & 7);
+            const int n = (r < An) ? aidx_s[r] : -1;
+            const uint32_t off = (n >= 0) ? static_cast<uint32_t>(n) * (kD * 2) + 16 * kpiece : kSkip;
+            const uint4 kr = *reinterpret_cast<const uint4*>(stash + swz(r, kpiece));
+            const uint4 vr = *reinterpret_cast<const uint4*>(stash + A * kD * 2 + swz(r, kpiece));
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, kr), rk, off, 0,
+                                                   kStreamPolicy);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vr), rv, off, 0,
+                                                   kStreamPolicy);
+        }
     }
 
     // Finalise: lane holds O[query 16qt + m16][16dt + 4g + i] = oacc[qt][dt][i]
@@ -1262,6 +1302,18 @@ int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
                            units, H, N, A, Nc, n_groups, scale_log2, active_idx, ld_act,
                            err_count, a_len, c_len);
         return status_from_launch();
+    }
+    // The fused update stashes the active rows in LDS when the stash still
+    // leaves room for two waves per SIMD (8 one-wave workgroups per CU).
+    const size_t lds_stash = lds + static_cast<size_t>(A) * kD * 2 * 2;
+    if constexpr (UPDATE) {
+        if (a_len == nullptr && n_groups == 1 && lds_stash <= kStashLdsMax) {
+            hipLaunchKernelGGL((attn_mfma_kernel<NQT, true, false, false, 1, true>), dim3(grid),
+                               dim3(64), lds_stash, stream, q_a, k_a, v_a, k_cache, v_cache,
+                               cached_idx, ldc, out, lse, units, H, N, A, Nc, n_groups,
+                               scale_log2, active_idx, ld_act, err_count, a_len, c_len);
+            return status_from_launch();
+        }
     }
     if (a_len != nullptr)
         hipLaunchKernelGGL((attn_mfma_kernel<NQT, UPDATE, true, false>), dim3(grid), dim3(64), lds,
