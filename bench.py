@@ -6,12 +6,16 @@ CFG = 128 sequences, 16 heads x 64, N = 320 tokens, active 48 = 16 generating
 
   * the host step plan (refresh decision, budget-filled K);
   * layer 2: refresh scores + top-K + active/cached partition (mar_refresh_topk);
-  * layers 3..32 (30 layers): cache-aware attention (mar_cache_attn_fwd) and the
-    K/V scatter of the active rows into that layer's cache (mar_kv_scatter_refresh),
-    the scatters on a second stream so they overlap the following layers'
-    attention (they touch rows no later layer reads);
+  * layers 3..32 (30 layers): cache-aware attention fused with the cache update
+    of the active rows (mar_cache_attn_fwd_update: one operator reads the fresh
+    active rows and the stored cached rows, merges the two softmax sums, and
+    writes the fresh rows into that layer's cache);
   * the CFG condition cache reuse on the 16-channel token outputs (mar_cfg_residual);
   * one cosine-gate evaluation on the 1024-wide hidden features (mar_cos_gate).
+
+The same step with the attention (mar_cache_attn_fwd) and the K/V scatter
+(mar_kv_scatter_refresh, on a second stream) as separate kernels is timed
+beside it (`unfused_step`).
 
 Every layer owns distinct Q/K/V and cache buffers (about 6.5 GB in all), so the
 256 MB Infinity Cache cannot serve one layer's data to the next.  Inputs are
@@ -19,9 +23,9 @@ seeded synthetic tensors already resident in HBM.
 
 Prints ONE JSON line.  `value` = active-query tokens per second through the
 cache-aware layers (128 x 48 x 30 per step / step time).  `roofline` describes
-the dominant kernel (the cache-aware attention); its average launch duration is
-measured with HIP events on the launch stream around the 30 back-to-back
-attention launches of each timed step.
+the dominant kernel of the step (the fused cache-aware attention + cache
+update); its average launch duration is measured with HIP events on the
+launch stream around groups of 30 back-to-back launches.
 """
 from __future__ import annotations
 
@@ -51,12 +55,20 @@ def attn_bytes(B, H, A, Nc, D, elem=2):
     return B * H * (4 * A + 2 * Nc) * D * elem + B * Nc * 4
 
 
+def fused_bytes(B, H, A, Nc, D, elem=2):
+    """Algorithmic bytes of one fused call (attention + cache update of the
+    active rows): the attention's bytes plus the A fresh K and V rows written
+    into the caches (they were already read for the attention)."""
+    return attn_bytes(B, H, A, Nc, D, elem) + 2 * B * H * A * D * elem
+
+
 def headline_record(cfg, n_ca, steps, warmup, ms_per_step, achieved_gbs, traffic, cpu):
     """The required part of the one-line JSON record.  `value` is active-query
     tokens per second of the whole step: B x A queries in each of the n_ca
-    cache-aware layers, over the step time.  `roofline` is that of the
-    cache-aware attention kernel: `achieved_gbs` is its algorithmic bytes per
-    launch over its measured launch time, against the HBM peak."""
+    cache-aware layers, over the step time.  `roofline` is that of the step's
+    dominant kernel, the fused cache-aware attention + cache update:
+    `achieved_gbs` is its algorithmic bytes per launch over its measured
+    launch time, against the HBM peak."""
     tokens_per_step = cfg.B * cfg.A * n_ca
     return {
         "metric": METRIC, "value": tokens_per_step / (ms_per_step * 1e-3), "unit": "tok/s",
@@ -98,8 +110,9 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(calls_bytes):
-    """Counter-measured HBM bytes per attention launch, if taken on this kernel source."""
+def load_traffic(kind):
+    """Counter-measured HBM bytes per launch of the kernel `kind` ("fused" or
+    "attention"), if the counters were taken on this kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -107,7 +120,7 @@ def load_traffic(calls_bytes):
         return None
     if t.get("kernel_source_sha256_16") != source_hash(ATTN_SRC):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("kernels", {}).get(kind, {}).get("hbm_bytes_per_launch")
 
 
 def cpu_model():
@@ -609,10 +622,10 @@ def main():
         """A whole 64-step decode of the attention path.  With the cache: on a
         refresh step (t mod 3 = 0) every layer runs full attention and rewrites
         its cache, and the CFG residual is stored; on the other steps layers 1-2
-        run full attention and layers 3-32 run the cached step above.  With the
-        condition cache as well, those other steps compute the conditional
-        branch only (half the sequences) and take the unconditional output from
-        the stored residual.  Without the cache every layer of every step runs
+        run full attention and layers 3-32 the fused cached layers of the step
+        above.  With the condition cache as well, those other steps compute the
+        conditional branch only (half the sequences) and take the unconditional
+        output from the stored residual.  Without the cache every layer of every step runs
         full attention."""
         for t in range(cfg.steps):
             if not use_cache:
@@ -632,7 +645,8 @@ def main():
             full_attn(0)
             full_attn(1)
             topk(plan)
-            cached_layers(plan)
+            for l in range(n_ca):
+                fused(l, plan)
             cfg_reuse()
             gate()
             X[0] = x
@@ -675,34 +689,36 @@ def main():
 
     print("bench: warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        one_step()
+        one_step_fused()
     torch.cuda.synchronize()
 
-    # Timed region 1: whole steps, no per-kernel events.
+    # Timed region 1: whole steps (fused attention + cache update), no
+    # per-kernel events.
     print("bench: timing steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     s0, s1 = ev(), ev()
     t0 = time.perf_counter()
     s0.record(stream)
     for _ in range(args.steps):
-        one_step()
+        one_step_fused()
     s1.record(stream)
     issue = time.perf_counter() - t0  # host time to issue the steps (no wait)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = s0.elapsed_time(s1) / args.steps
 
-    # Timed region 1b: whole steps with the fused attention + cache update.
+    # Timed region 1b: whole steps with attention and scatter as separate
+    # kernels (the scatters on the side stream).
     for _ in range(args.warmup):
-        one_step_fused()
+        one_step()
     torch.cuda.synchronize()
     f0, f1 = ev(), ev()
     f0.record(stream)
     for _ in range(args.steps):
-        one_step_fused()
+        one_step()
     f1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step_fused = f0.elapsed_time(f1) / args.steps
+    ms_per_step_unfused = f0.elapsed_time(f1) / args.steps
 
     # Timed region 2: the same launches, grouped per kernel, HIP events per group.
     # Timed before the decodes, whose second of heavy load slows later groups.
@@ -749,11 +765,9 @@ def main():
 
 
     tokens_per_step = cfg.B * cfg.A * n_ca
-    value = tokens_per_step / (ms_per_step * 1e-3)
     bytes_call = attn_bytes(cfg.B, cfg.H, cfg.A, cfg.Nc, cfg.D)
     achieved = bytes_call / (avg_us["attn"] * 1e-6) / 1e9
-    traffic = load_traffic(bytes_call)
-    bytes_fused = bytes_call + 2 * cfg.B * cfg.H * cfg.A * cfg.D * 2  # + K_A, V_A rows written
+    bytes_fused = fused_bytes(cfg.B, cfg.H, cfg.A, cfg.Nc, cfg.D)
     achieved_fused = bytes_fused / (avg_us["attn_update"] * 1e-6) / 1e9
 
     full_flops = 4 * cfg.B * cfg.H * cfg.N * cfg.N * cfg.D
@@ -783,17 +797,23 @@ def main():
         print("bench: oracle CPU baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(x, cfg.Nc, cfg, args)
 
-    line = headline_record(cfg, n_ca, args.steps, args.warmup, ms_per_step, achieved, traffic, cpu)
+    line = headline_record(cfg, n_ca, args.steps, args.warmup, ms_per_step, achieved_fused,
+                           load_traffic("fused"), cpu)
+    line["roofline"].update({"kernel": "mar_cache_attn_fwd_update (attention + cache update)",
+                             "bytes_per_call": bytes_fused,
+                             "us_per_call": avg_us["attn_update"]})
     line.update({
         "kernel_us": avg_us,
-        "fused_step": {
-            "what": "the same step with mar_cache_attn_fwd_update (attention + cache update of "
-                    "the active rows in one kernel) in place of attention + scatter",
-            "ms_per_step": ms_per_step_fused,
-            "value": tokens_per_step / (ms_per_step_fused * 1e-3),
-            "roofline": {"bound": "hbm", "achieved": achieved_fused, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": achieved_fused / PEAK_HBM_GBS,
-                         "bytes_per_call": bytes_fused}},
+        "attention_roofline": {
+            "what": "the cache-aware attention alone (mar_cache_attn_fwd), same layers",
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": load_traffic("attention"),
+            "bytes_per_call": bytes_call, "us_per_call": avg_us["attn"]},
+        "unfused_step": {
+            "what": "the same step with mar_cache_attn_fwd + mar_kv_scatter_refresh (the "
+                    "scatters on a second stream) in place of the fused kernel",
+            "ms_per_step": ms_per_step_unfused,
+            "value": tokens_per_step / (ms_per_step_unfused * 1e-3)},
         "full_attention": {
             "what": "mar_cache_attn_fwd with A = N and no cached rows (layers 1-2 of every "
                     "step, every layer of a refresh step), outside the step above",
@@ -828,6 +848,7 @@ def main():
         "locality": loc,
         "attn_median_us": attn_median_us,
         "attn_frac_of_copy": (achieved / copy_gbs) if copy_gbs else None,
+        "fused_frac_of_copy": (achieved_fused / copy_gbs) if copy_gbs else None,
         "attn_bytes_per_call": bytes_call,
         "attn_tok_per_s": cfg.B * cfg.A / (avg_us["attn"] * 1e-6),
         "copy_gbs": copy_gbs,

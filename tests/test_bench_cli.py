@@ -35,6 +35,9 @@ def test_attention_algorithmic_bytes():
     assert b.attn_bytes(128, 16, 48, 272, 64) == 193077248
     # fp32 doubles the row bytes, not the list
     assert b.attn_bytes(1, 1, 8, 56, 64, elem=4) == (4 * 8 + 2 * 56) * 64 * 4 + 56 * 4
+    # the fused call also writes the 48 fresh K and V rows into the caches
+    assert b.fused_bytes(128, 16, 48, 272, 64) == 193077248 + 2 * 128 * 16 * 48 * 64 * 2
+    assert b.fused_bytes(128, 16, 48, 272, 64) == 218243072
 
 
 def test_traffic_only_for_the_measured_source(tmp_path):
@@ -43,15 +46,17 @@ def test_traffic_only_for_the_measured_source(tmp_path):
     src.write_text("// kernel v1\n")
     rec = tmp_path / "traffic.json"
     rec.write_text(json.dumps({"kernel_source_sha256_16": b.source_hash(str(src)),
-                               "hbm_bytes_per_launch": 123.0}))
+                               "kernels": {"fused": {"hbm_bytes_per_launch": 123.0},
+                                           "attention": {"hbm_bytes_per_launch": 45.0}}}))
     b.TRAFFIC_FILE, b.ATTN_SRC = str(rec), str(src)
-    assert b.load_traffic(1) == 123.0
+    assert b.load_traffic("fused") == 123.0 and b.load_traffic("attention") == 45.0
+    assert b.load_traffic("other") is None
     src.write_text("// kernel v2\n")  # the source changed since the counters were taken
-    assert b.load_traffic(1) is None
+    assert b.load_traffic("fused") is None
     rec.write_text("not json")
-    assert b.load_traffic(1) is None
+    assert b.load_traffic("fused") is None
     os.remove(rec)
-    assert b.load_traffic(1) is None
+    assert b.load_traffic("fused") is None
 
 
 
