@@ -237,12 +237,13 @@ def build_inputs(cfg, dev):
         "clen": torch.empty((cfg.B,), dtype=torch.int32, device=dev),
         "full_out": torch.empty((cfg.B, cfg.H, cfg.N, cfg.D), dtype=torch.bfloat16, device=dev),
     }
+    x["partials"] = x["workspace"].view(cfg.B, cfg.H, cfg.N)
     torch.cuda.synchronize()
     return x
 
 
 SEQ_KEYS = ("gp", "q_gen", "k_full", "scores", "active_idx", "cached_idx", "cached_len",
-            "gate_x", "gate_y", "cos", "reuse", "cidx", "clen", "full_out")
+            "gate_x", "gate_y", "cos", "reuse", "cidx", "clen", "full_out", "partials")
 
 
 def seq_view(x, nb):
@@ -486,6 +487,15 @@ def main():
     print(f"bench: building MAR-L inputs ({cfg.layers - 2} cache-aware layers)", file=sys.stderr,
           flush=True)
     x = build_inputs(cfg, dev)
+    # layer 2 in two passes needs the generating rows of each layer's queries
+    # (layer l + 1's K stands in for layer l's queries) as their own tensor
+    n_layers = cfg.layers - 2
+    gen_pos = x["gp"][:, cfg.n_prev:cfg.n_prev + cfg.n_gen].long()
+    gidx = gen_pos[:, None, :, None].expand(cfg.B, cfg.H, cfg.n_gen, cfg.D)
+    for l in range(n_layers):
+        Lq = x["layers"][(l + 1) % n_layers]["k_cache"]
+        x["layers"][l]["q_gen2"] = torch.gather(Lq, 2, gidx).contiguous()
+    torch.cuda.synchronize()
     counts = [cfg.n_gen] * (cfg.steps)
     counts[0] = 0
     # the whole decode follows the cosine masking schedule over the 256 image tokens
@@ -569,6 +579,33 @@ def main():
         prepared(("full", l), marca.mar_cache_attn_fwd, Lq["k_cache"], L["k_cache"], L["v_cache"],
                  L["k_cache"], L["v_cache"], None, Nc=0, out=x["full_out"], stream=stream)()
 
+    def layer2_separate(l, plan):
+        """Layer 2 of a cached step as two passes over its K: the full
+        attention (layer l's buffers), then the refresh scores + top-K of
+        mar_refresh_topk on the generating rows of the same queries."""
+        x = X[0]
+        L = x["layers"][l]
+        full_attn(l)
+        prepared(("l2topk", l, plan.n_prev + plan.n_gen, plan.n_refresh), marca.mar_refresh_topk,
+                 L["q_gen2"], L["k_cache"], x["gp"], plan.n_prev + plan.n_gen, plan.n_refresh,
+                 scores=x["scores"], active_idx=x["active_idx"], cached_idx=x["cached_idx"],
+                 cached_len=x["cached_len"], workspace=x["workspace"], stream=stream)()
+
+    def layer2_fused(l, plan):
+        """Layer 2 of a cached step in one pass over its K: the full attention
+        that also writes the generating queries' per-head probability sums,
+        then the selection from them."""
+        x = X[0]
+        L, Lq = x["layers"][l], x["layers"][(l + 1) % n_ca]
+        gen = x["gp"][:, plan.n_prev:plan.n_prev + plan.n_gen]
+        prepared(("l2scores", l, plan.n_prev, plan.n_gen), marca.mar_cache_attn_fwd_scores,
+                 Lq["k_cache"], L["k_cache"], L["v_cache"], gen, plan.n_gen,
+                 partials=x["partials"], out=x["full_out"], stream=stream)()
+        prepared(("l2select", plan.n_prev + plan.n_gen, plan.n_refresh, plan.n_gen),
+                 marca.mar_refresh_select, x["partials"], x["gp"], plan.n_prev + plan.n_gen,
+                 plan.n_refresh, plan.n_gen, scores=x["scores"], active_idx=x["active_idx"],
+                 cached_idx=x["cached_idx"], cached_len=x["cached_len"], stream=stream)()
+
     def cfg_reuse():
         prepared(("cfg_reuse",), marca.mar_cfg_residual, x["cond"], residual=x["residual"],
                  mode=marca.MAR_CFG_REUSE, uncond_out=x["uncond_out"], stream=stream)()
@@ -625,7 +662,9 @@ def main():
         run full attention and layers 3-32 the fused cached layers of the step
         above.  With the condition cache as well, those other steps compute the
         conditional branch only (half the sequences) and take the unconditional
-        output from the stored residual.  Without the cache every layer of every step runs
+        output from the stored residual.  On a cached step layer 2's attention
+        also yields the refresh scores (mar_cache_attn_fwd_scores) and the
+        selection reads them (mar_refresh_select).  Without the cache every layer of every step runs
         full attention."""
         for t in range(cfg.steps):
             if not use_cache:
@@ -643,8 +682,7 @@ def main():
             if cond_cache:
                 X[0] = x_cond
             full_attn(0)
-            full_attn(1)
-            topk(plan)
+            layer2_fused(1, plan)
             for l in range(n_ca):
                 fused(l, plan)
             cfg_reuse()
@@ -685,6 +723,8 @@ def main():
         span("full_refresh", lambda: [full_refresh(l) for l in range(n_ca)], n_ca)
         span("attn_pattern", lambda: [pattern(l, True) for l in range(n_ca)], n_ca)
         span("attn_pattern_reads", lambda: [pattern(l, False) for l in range(n_ca)], n_ca)
+        span("layer2_separate", lambda: [layer2_separate(l, plan) for l in range(n_ca)], n_ca)
+        span("layer2_fused", lambda: [layer2_fused(l, plan) for l in range(n_ca)], n_ca)
         return spans
 
     print("bench: warmup", file=sys.stderr, flush=True)
@@ -845,6 +885,13 @@ def main():
             "us_per_call": avg_us["attn_pattern"],
             "reads_only_us_per_call": avg_us["attn_pattern_reads"],
             "attn_over_pattern": avg_us["attn"] / avg_us["attn_pattern"]},
+        "layer2": {
+            "what": "layer 2 of a cached step (full attention over 320 tokens + the refresh "
+                    "top-K): as the full attention then mar_refresh_topk (which reads K again), "
+                    "and as mar_cache_attn_fwd_scores (the attention also sums the generating "
+                    "queries' probabilities per head) then mar_refresh_select; per layer-2 call",
+            "separate_us": avg_us["layer2_separate"], "fused_us": avg_us["layer2_fused"],
+            "saved_us": avg_us["layer2_separate"] - avg_us["layer2_fused"]},
         "locality": loc,
         "attn_median_us": attn_median_us,
         "attn_frac_of_copy": (achieved / copy_gbs) if copy_gbs else None,

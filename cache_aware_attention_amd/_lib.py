@@ -67,6 +67,10 @@ def load_library(path: Optional[str] = None):
     lib.mar_cache_attn_fwd_update.restype = I
     lib.mar_cache_attn_fwd_update.argtypes = [V, V, V, V, V, V, I, V, I, V, V, V, I, I, I, I, I,
                                               I, F, I, V]
+    lib.mar_cache_attn_fwd_scores.restype = I
+    lib.mar_cache_attn_fwd_scores.argtypes = [V, V, V, V, V, V, I, I, V, S, I, I, I, I, F, I, V]
+    lib.mar_refresh_select.restype = I
+    lib.mar_refresh_select.argtypes = [V, S, V, I, I, I, V, V, I, V, I, V, I, I, I, I, V]
     lib.mar_kv_scatter_refresh.restype = I
     lib.mar_kv_scatter_refresh.argtypes = [V, V, V, V, V, I, V, I, I, I, I, I, I, V]
     lib.mar_refresh_topk_workspace.restype = S
@@ -367,6 +371,68 @@ def mar_refresh_topk(q_gen, k_full, gp_idx, n_gp, K, scores=None, active_idx=Non
         _dev(cached_idx, "cached_idx", torch.int32), cached_idx.shape[1],
         _dev(cached_len, "cached_len"), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), B, H, G, N, D, code, _stream(stream))
+    return scores, active_idx, cached_idx, cached_len
+
+
+def mar_cache_attn_fwd_scores(q, k, v, gen_idx, G, partials=None, out=None, lse=None,
+                              scale=None, stream=None):
+    """Layer 2's full attention over all N tokens that also writes the per-head
+    sums of the G generating queries' probabilities (see mar_cache_attn.h).
+    gen_idx [B, ld_gen] int32.  Returns (out [B,H,N,D], partials [B,H,N] float32)."""
+    B, H, N, D = q.shape
+    dt = q.dtype
+    for name, t in (("k", k), ("v", v)):
+        _dev(t, name, dt, (B, H, N, D))
+    if gen_idx.dim() != 2 or gen_idx.shape[0] != B or gen_idx.stride(1) != 1:
+        raise ValueError("gen_idx must be [B, ld_gen] with contiguous rows")
+    if not gen_idx.is_cuda or gen_idx.dtype != torch.int32:
+        raise ValueError("gen_idx must be a GPU int32 tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dt, (B, H, N, D))
+    if partials is None:
+        partials = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _dev(partials, "partials", torch.float32, (B, H, N))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, H, N))
+    _call("mar_cache_attn_fwd_scores", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+          _dev(lse, "lse") if lse is not None else None, ctypes.c_void_p(gen_idx.data_ptr()),
+          gen_idx.stride(0), int(G), _dev(partials, "partials"), partials.numel() * 4, B, H, N, D,
+          float(D ** -0.5 if scale is None else scale), _dtype_code(q), _stream(stream))
+    return out, partials
+
+
+def mar_refresh_select(partials, gp_idx, n_gp, K, G, scores=None, active_idx=None,
+                       cached_idx=None, cached_len=None, stream=None):
+    """The selection half of mar_refresh_topk from per-head partials [B,H,N]
+    (mar_cache_attn_fwd_scores writes them).  Returns (scores, active_idx,
+    cached_idx, cached_len) as mar_refresh_topk does."""
+    B, H, N = partials.shape
+    _dev(partials, "partials", torch.float32, (B, H, N))
+    dev = partials.device
+    if gp_idx is None:
+        ld_gp, gp_ptr = 0, None
+    else:
+        if gp_idx.dim() != 2 or gp_idx.shape[0] != B or gp_idx.stride(1) != 1:
+            raise ValueError("gp_idx must be [B, ld_gp] with contiguous rows")
+        if not gp_idx.is_cuda or gp_idx.dtype != torch.int32:
+            raise ValueError("gp_idx must be a GPU int32 tensor")
+        ld_gp, gp_ptr = gp_idx.stride(0), ctypes.c_void_p(gp_idx.data_ptr())
+    if scores is None:
+        scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if active_idx is None:
+        active_idx = torch.empty((B, max(n_gp + K, 1)), dtype=torch.int32, device=dev)
+    if cached_idx is None:
+        cached_idx = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if cached_len is None:
+        cached_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    _dev(scores, "scores", torch.float32, (B, N))
+    _dev(cached_len, "cached_len", torch.int32, (B,))
+    _call("mar_refresh_select", _dev(partials, "partials"), partials.numel() * 4, gp_ptr, ld_gp,
+          int(n_gp), int(K), _dev(scores, "scores"),
+          _dev(active_idx, "active_idx", torch.int32), active_idx.shape[1],
+          _dev(cached_idx, "cached_idx", torch.int32), cached_idx.shape[1],
+          _dev(cached_len, "cached_len"), B, H, int(G), N, _stream(stream))
     return scores, active_idx, cached_idx, cached_len
 
 

@@ -99,6 +99,21 @@ extern "C" int mar_cache_attn_fwd_update(const void* q_a, const void* k_a, const
                                            Nc, scale, dtype, stream);
 }
 
+extern "C" int mar_cache_attn_fwd_scores(const void* q, const void* k, const void* v, void* out,
+                                         float* lse, const int32_t* gen_idx, int ld_gen, int G,
+                                         float* partials, size_t partials_bytes, int B, int H,
+                                         int N, int D, float scale, int dtype, void* stream) {
+    const int st = check_cache_attn(q, k, v, k, v, nullptr, 0, out, B, H, N, N, 0, D, scale,
+                                    dtype);
+    if (st != MAR_OK) return st;
+    if (!gen_idx || !partials) return MAR_E_NULL;
+    if (G < 1 || ld_gen < G) return MAR_E_SHAPE;
+    if (dtype != MAR_BF16 || N <= 64 || N > 320 || G > 16) return MAR_E_UNSUPPORTED;
+    if (partials_bytes < (size_t)B * H * N * sizeof(float)) return MAR_E_WORKSPACE;
+    return marca::launch_cache_attn_scores(q, k, v, out, lse, gen_idx, ld_gen, G, partials, B, H,
+                                           N, scale, stream);
+}
+
 extern "C" int mar_kv_scatter_refresh(void* k_cache, void* v_cache, const void* k_new,
                                       const void* v_new, const int32_t* idx, int ld_idx,
                                       int32_t* err_count, int B, int H, int N, int M, int D,
@@ -159,6 +174,25 @@ extern "C" int mar_refresh_topk(const void* q_gen, const void* k_full, const int
     return marca::launch_refresh_topk(q_gen, k_full, gp_idx, ld_gp, n_gp, K, scale, scores,
                                       active_idx, ld_act, cached_idx, ld_cached, cached_len,
                                       static_cast<float*>(workspace), B, H, G, N, dtype, stream);
+}
+
+extern "C" int mar_refresh_select(const float* partials, size_t partials_bytes,
+                                  const int32_t* gp_idx, int ld_gp, int n_gp, int K,
+                                  float* scores, int32_t* active_idx, int ld_act,
+                                  int32_t* cached_idx, int ld_cached, int32_t* cached_len, int B,
+                                  int H, int G, int N, void* stream) {
+    if (!partials || !scores || !active_idx || !cached_idx || !cached_len) return MAR_E_NULL;
+    if (n_gp > 0 && !gp_idx) return MAR_E_NULL;
+    if (B < 1 || H < 1 || G < 1 || N < 1 || n_gp < 0) return MAR_E_SHAPE;
+    if (K < 0 || (long long)n_gp + K > N) return MAR_E_RANGE;
+    if (n_gp > 0 && ld_gp < n_gp) return MAR_E_SHAPE;
+    if (ld_act < n_gp + K || ld_act < 1) return MAR_E_SHAPE;
+    if (ld_cached < N - n_gp - K || ld_cached < 1) return MAR_E_SHAPE;
+    if (N > kMaxTopkTokens) return MAR_E_UNSUPPORTED;
+    if (partials_bytes < mar_refresh_topk_workspace(B, H, N)) return MAR_E_WORKSPACE;
+    return marca::launch_refresh_select(partials, gp_idx, ld_gp, n_gp, K, scores, active_idx,
+                                        ld_act, cached_idx, ld_cached, cached_len, B, H, G, N,
+                                        stream);
 }
 
 extern "C" int mar_refresh_topk_noalloc(const void* q_gen, const void* k_full,

@@ -794,7 +794,18 @@ constexpr int kWgWaves = 4;
 constexpr int kWgNqt = 5;
 constexpr int kWgTile = kChunk * 128;  // bytes of one K or V chunk tile
 
-template <int NQT, int W, bool UPDATE, bool CACHED, bool RAGGED = false>
+//  * SCORES (no cached rows, no update, one workgroup per unit of at most 320
+//    tokens: layer 2's full attention on a cached step): every K chunk stays
+//    in LDS (at its own slot instead of the double buffer) and each query's
+//    reference is recorded; after the last chunk the waves score the unit's
+//    generating queries (gen_idx, at most 16) against the K held in LDS and
+//    write their softmax probabilities summed over those queries, per key --
+//    the per-head partials the refresh selection reads ("MARche" paper-notes
+//    page, Key Design 1: the top-K reads layer 2's attention from the
+//    generating tokens; without this the scores kernel reads K again).  The
+//    probabilities are exp2(s c - m) / l in fp32 with the query's attention
+//    reference m and l their exact fp32 sum over the keys.
+template <int NQT, int W, bool UPDATE, bool CACHED, bool RAGGED = false, bool SCORES = false>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
                     const uint16_t* __restrict__ v_a, uint16_t* k_cache, uint16_t* v_cache,
@@ -803,9 +814,12 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
                     int ldc, int H, int N, int Nc, const int32_t* __restrict__ active_idx,
                     int ld_act, int32_t* __restrict__ err_count,
                     const int32_t* __restrict__ a_len = nullptr,
-                    const int32_t* __restrict__ c_len = nullptr) {
+                    const int32_t* __restrict__ c_len = nullptr,
+                    const int32_t* __restrict__ gen_idx = nullptr, int ld_gen = 0, int G = 0,
+                    float* __restrict__ partials = nullptr) {
     static_assert(W == 1 || W == 2 || W == 4, "waves per workgroup");
     static_assert(!RAGGED || (CACHED && !UPDATE), "per-sequence counts: cached rows, no update");
+    static_assert(!SCORES || (!CACHED && !UPDATE && W == 4), "scores: layer 2's full attention");
     constexpr int kQ = 16 * NQT;         // queries per wave
     constexpr int kPasses = 4 / W;       // load passes per chunk (8 W rows each)
     // The chunk loads (whole rows, 8 lanes per row): streaming with cached
@@ -890,11 +904,17 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
             }
         }
     };
+    // SCORES: K chunk c at its own slot of the dynamic LDS, kall + c * kWgTile.
+    unsigned char* kall = reinterpret_cast<unsigned char*>(wg_lists);
     auto put = [&](int buf, int c, const uint4 (&kk)[kPasses], const uint4 (&vv)[kPasses]) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
             const int lofs = swz(8 * W * p + lrow, tid & 7);
-            *reinterpret_cast<uint4*>(lds + buf * 2 * kWgTile + lofs) = kk[p];
+            if constexpr (SCORES) {
+                if (c < nchunks) *reinterpret_cast<uint4*>(kall + c * kWgTile + lofs) = kk[p];
+            } else {
+                *reinterpret_cast<uint4*>(lds + buf * 2 * kWgTile + lofs) = kk[p];
+            }
             *reinterpret_cast<uint4*>(lds + buf * 2 * kWgTile + kWgTile + lofs) = vv[p];
         }
         if constexpr (UPDATE) {
@@ -964,8 +984,8 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     auto compute = [&](int c, int buf, uint32_t rows, auto full_tag, auto first_tag) __attribute__((always_inline)) {
         constexpr bool kFull = decltype(full_tag)::value;    // every row of the chunk exists
         constexpr bool kFirst = decltype(first_tag)::value;  // chunk 0: sets the references
-        const unsigned char* kt = lds + buf * 2 * kWgTile;
-        const unsigned char* vt = kt + kWgTile;
+        const unsigned char* kt = SCORES ? kall + c * kWgTile : lds + buf * 2 * kWgTile;
+        const unsigned char* vt = lds + buf * 2 * kWgTile + kWgTile;
         uint4 kop[2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -1202,10 +1222,20 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
         if (c < nchunks) step_any(c, B1{});
     }
 
+    if constexpr (SCORES) {
+        // The references of this wave's queries, for the scores below.
+        float* mq_s = reinterpret_cast<float*>(kall + nchunks * kWgTile);
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+            if (g == 0 && 16 * qt + m16 < nq) mq_s[q0 + 16 * qt + m16] = mc[qt];
+    }
+
     // Finalise through this wave's 2 KB of the (now free) LDS tiles, one
     // 16-query tile at a time, so that every (nontemporal) store writes
-    // whole 128-byte rows.
-    if (nq <= 0) return;
+    // whole 128-byte rows.  (SCORES: the output first, so its accumulators
+    // are free before the scores; a wave without queries stays for the
+    // barriers that follow.)
+    if (!SCORES && nq <= 0) return;
     unsigned char* ot = lds + w * 2048;
     u32x4_t* orow = reinterpret_cast<u32x4_t*>(out + ub + static_cast<size_t>(q0) * kD);
 #pragma unroll
@@ -1232,6 +1262,88 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
         }
         __builtin_amdgcn_wave_barrier();  // the reads before the next tile's writes
     }
+
+    if constexpr (SCORES) {
+        // References of this wave's queries, then the generating queries'
+        // probabilities against the K chunks held in LDS.  Lane (g, m16) holds
+        // S[generating query 4g + i][key 16t + m16] of key tile t (the scores
+        // kernel's layout: Q as the A operand, K as the B operand).
+        float* mq_s = reinterpret_cast<float*>(kall + nchunks * kWgTile);  // [nchunks * 32]
+        float* red_s = mq_s + nchunks * kChunk;                             // [W][16]
+        const int32_t* gi = gen_idx + static_cast<size_t>(u / H) * ld_gen;
+        const int gq = (m16 < G) ? gi[m16] : -1;  // this lane's A-operand query
+        const bool gq_ok = gq >= 0 && gq < A;
+        uint4 qlo = make_uint4(0, 0, 0, 0), qhi = qlo;
+        if (gq_ok) {
+            const uint4* pq = reinterpret_cast<const uint4*>(q_a + ub + static_cast<size_t>(gq) * kD);
+            qlo = pq[g];
+            qhi = pq[4 + g];
+        }
+        __syncthreads();  // the references are in LDS
+        float mg[4];
+        bool row_ok[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // the generating query of row 4g + i
+            const int r = 4 * g + i;
+            const int pos = (r < G) ? gi[r] : -1;
+            row_ok[i] = pos >= 0 && pos < A;
+            mg[i] = row_ok[i] ? mq_s[pos] : 0.f;
+        }
+        constexpr int kTiles = (5 * 64) / (16 * W);  // 16-key tiles per wave at 320 keys
+        const int ntiles = 2 * nchunks;
+        float e[kTiles][4];
+        float l[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < kTiles; ++k) {
+            const int t = w + W * k;  // uniform
+            const int key = 16 * t + m16;
+            f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+            if (t < ntiles) {
+                const unsigned char* kt = kall + (t >> 1) * kWgTile;
+                const int r = 16 * (t & 1) + m16;
+                const uint4 k0 = *reinterpret_cast<const uint4*>(kt + swz(r, g));
+                const uint4 k1 = *reinterpret_cast<const uint4*>(kt + swz(r, 4 + g));
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qlo), as_bf16x8(k0), sacc, 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qhi), as_bf16x8(k1), sacc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e[k][i] = (t < ntiles && key < A && row_ok[i])
+                              ? __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -mg[i]))
+                              : 0.f;
+                l[i] += e[k][i];
+            }
+        }
+        // Row sums: over the 16 lanes of a row, then over the waves in order.
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) l[i] += __shfl_xor(l[i], o, kWave);
+        if (m16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red_s[w * 16 + 4 * g + i] = l[i];
+        __syncthreads();
+        float inv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float t = red_s[4 * g + i];
+#pragma unroll
+            for (int v = 1; v < W; ++v) t += red_s[v * 16 + 4 * g + i];
+            inv[i] = row_ok[i] ? 1.f / t : 0.f;
+        }
+        // Per key: the probabilities summed over the generating queries.
+        float* pu = partials + static_cast<size_t>(u) * A;
+#pragma unroll
+        for (int k = 0; k < kTiles; ++k) {
+            float col = e[k][0] * inv[0];
+#pragma unroll
+            for (int i = 1; i < 4; ++i) col += e[k][i] * inv[i];
+            col += __shfl_xor(col, 16, kWave);
+            col += __shfl_xor(col, 32, kWave);
+            const int key = 16 * (w + W * k) + m16;
+            if (g == 0 && key < A) pu[key] = col;
+        }
+    }
 }
 
 template <bool UPDATE>
@@ -1246,6 +1358,23 @@ int launch_dense_wg(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_
     hipLaunchKernelGGL((attn_wg_kernel<kWgNqt, kWgWaves, UPDATE, false>), dim3(grid),
                        dim3(64 * kWgWaves), 0, stream, q_a, k_a, v_a, k_cache, v_cache, out, lse,
                        units, A, nb, scale_log2, nullptr, 0, H, A, 0, nullptr, 0, nullptr);
+    return status_from_launch();
+}
+
+// Layer 2's full attention with the refresh partials (SCORES): one workgroup
+// of 4 waves x 80 queries per unit of at most 320 tokens; dynamic LDS: the K
+// chunks, the query references and the cross-wave sums.
+int launch_scores_wg(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                     float* lse, const int32_t* gen_idx, int ld_gen, int G, float* partials,
+                     int B, int H, int N, float scale_log2, hipStream_t stream) {
+    const int units = B * H;
+    const int nchunks = (N + kChunk - 1) / kChunk;
+    const size_t lds = static_cast<size_t>(nchunks) * kWgTile + static_cast<size_t>(nchunks) * kChunk * 4 +
+                       kWgWaves * 16 * 4;
+    hipLaunchKernelGGL((attn_wg_kernel<kWgNqt, kWgWaves, false, false, false, true>), dim3(units),
+                       dim3(64 * kWgWaves), lds, stream, q, k, v, const_cast<uint16_t*>(k),
+                       const_cast<uint16_t*>(v), out, lse, units, N, 1, scale_log2, nullptr, 0, H,
+                       N, 0, nullptr, 0, nullptr, nullptr, nullptr, gen_idx, ld_gen, G, partials);
     return status_from_launch();
 }
 
@@ -1518,6 +1647,15 @@ int launch_cache_attn_ragged(const void* q_a, const void* k_a, const void* v_a,
                              int dtype, void* stream_v) {
     return launch_attn_impl(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse, B, H, N,
                             A, Nc, scale, dtype, a_len, c_len, stream_v);
+}
+
+int launch_cache_attn_scores(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const int32_t* gen_idx, int ld_gen, int G, float* partials, int B,
+                             int H, int N, float scale, void* stream_v) {
+    return launch_scores_wg(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse,
+                            gen_idx, ld_gen, G, partials, B, H, N, scale * kLog2e,
+                            static_cast<hipStream_t>(stream_v));
 }
 
 int launch_cache_attn_update(const void* q_a, const void* k_a, const void* v_a, void* k_cache,

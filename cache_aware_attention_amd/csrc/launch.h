@@ -28,6 +28,12 @@ int launch_cache_attn_update(const void* q_a, const void* k_a, const void* v_a, 
                              float* lse, int B, int H, int N, int A, int Nc, float scale,
                              int dtype, void* stream);
 
+// Layer 2's full attention (A = N <= 320, no cached rows, bf16) that also
+// writes the generating queries' per-head probability sums into partials.
+int launch_cache_attn_scores(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const int32_t* gen_idx, int ld_gen, int G, float* partials, int B,
+                             int H, int N, float scale, void* stream);
+
 int launch_kv_scatter(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                       const int32_t* idx, int ld_idx, int32_t* err_count,
                       int B, int H, int N, int M, int row_bytes, void* stream);
@@ -38,6 +44,12 @@ int launch_refresh_topk(const void* q_gen, const void* k_full,
                         int32_t* cached_idx, int ld_cached, int32_t* cached_len,
                         float* workspace, int B, int H, int G, int N, int dtype,
                         void* stream);
+
+// The selection half of launch_refresh_topk, from per-head partials [B,H,N].
+int launch_refresh_select(const float* partials, const int32_t* gp_idx, int ld_gp, int n_gp,
+                          int K, float* scores, int32_t* active_idx, int ld_act,
+                          int32_t* cached_idx, int ld_cached, int32_t* cached_len, int B, int H,
+                          int G, int N, void* stream);
 
 // The allocation-free top-K: the partial scores go to the library's own
 // per-device array of kTopkScratchBytes (B*H*N floats must fit; checked by

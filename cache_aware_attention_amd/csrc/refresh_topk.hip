@@ -667,8 +667,17 @@ int launch_refresh_topk(const void* q_gen, const void* k_full, const int32_t* gp
                            static_cast<const float*>(q_gen), static_cast<const float*>(k_full),
                            workspace, G, N, scale_log2);
     }
-    int st = status_from_launch();
+    const int st = status_from_launch();
     if (st != MAR_OK) return st;
+    return launch_refresh_select(workspace, gp_idx, ld_gp, n_gp, K, scores, active_idx, ld_act,
+                                 cached_idx, ld_cached, cached_len, B, H, G, N, stream_v);
+}
+
+int launch_refresh_select(const float* workspace, const int32_t* gp_idx, int ld_gp, int n_gp,
+                          int K, float* scores, int32_t* active_idx, int ld_act,
+                          int32_t* cached_idx, int ld_cached, int32_t* cached_len, int B, int H,
+                          int G, int N, void* stream_v) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
     const size_t lds2 = (size_t)N * sizeof(uint64_t) + (size_t)N;
     const float inv_hg = 1.f / (float)(H * G);
 #define MARCA_SELECT(NB)                                                                     \

@@ -154,6 +154,34 @@ int mar_cache_attn_fwd_update(const void* q_a, const void* k_a, const void* v_a,
                               float scale, int dtype, void* stream);
 
 /*
+ * Layer-2 full attention that also emits the refresh relevance partials
+ * ([MARche] Key Design 1 and figure 3 on the Pith page: the refreshing tokens
+ * are ranked by layer 2's attention from the generating tokens to every
+ * token, averaged over heads; Overall Architecture: one fused operator).
+ *
+ * Computes what mar_cache_attn_fwd computes for a full-attention layer
+ * (A == N, no cached rows; out and lse as there), and in the same pass
+ *   partials[(b*H + h)*N + j] = sum over g < G of
+ *       softmax_j(scale * <q[b,h,gen_idx[b*ld_gen + g],:], k[b,h,j,:]>)
+ * -- the per-head sums of the generating queries' probabilities that
+ * mar_refresh_select turns into scores and the active / cached partition, so
+ * that the selection does not read K again.
+ *   q, k, v     [B,H,N,D]   layer 2's queries, keys and values of all N tokens
+ *   out         [B,H,N,D];  lse [B,H,N] float, may be NULL
+ *   gen_idx     [B,ld_gen] int32: the G generating tokens' positions; an entry
+ *               outside [0,N) contributes nothing
+ *   partials    [B,H,N] float, partials_bytes >= B*H*N*4 (MAR_E_WORKSPACE)
+ * Requires bf16 (MAR_E_UNSUPPORTED otherwise), D == 64, 64 < N <= 320,
+ * 1 <= G <= 16, ld_gen >= G; scale positive and finite.  The probabilities
+ * are fp32 and normalised by their exact fp32 sums.
+ */
+int mar_cache_attn_fwd_scores(const void* q, const void* k, const void* v,
+                              void* out, float* lse,
+                              const int32_t* gen_idx, int ld_gen, int G,
+                              float* partials, size_t partials_bytes,
+                              int B, int H, int N, int D, float scale, int dtype, void* stream);
+
+/*
  * KV cache update  ([MARche] abstract on the Pith page: only the tokens that
  * need recomputation are updated; Key Design 3 and flowchart: every 3rd step
  * a periodic full refresh rewrites the whole cache).
@@ -214,6 +242,27 @@ int mar_refresh_topk(const void* q_gen, const void* k_full,
                      int32_t* cached_idx, int ld_cached, int32_t* cached_len,
                      void* workspace, size_t ws_bytes,
                      int B, int H, int G, int N, int D, int dtype, void* stream);
+
+/*
+ * The selection half of mar_refresh_topk, from per-head partials such as
+ * mar_cache_attn_fwd_scores writes ([MARche] Key Design 1: the K highest
+ * head-averaged scores among the tokens outside G and P are refreshed;
+ * Overall Architecture: active = generating + previous + refreshing tokens).
+ *   partials [B,H,N] float: per (sequence, head, token) sums over the G
+ *            generating queries of their softmax probabilities
+ *   scores[b,j] = 1/(H*G) * sum_h partials[b,h,j]  (summed over h in order)
+ * and gp_idx, K, active_idx, cached_idx, cached_len exactly as in
+ * mar_refresh_topk (ties to the lower index; -1 where fewer than K tokens
+ * are eligible).  Requires partials_bytes >= B*H*N*4 (MAR_E_WORKSPACE),
+ * 1 <= G, 0 <= K, n_gp + K <= N, ld_gp >= n_gp, ld_act >= n_gp + K,
+ * ld_cached >= N - n_gp - K, N <= 4096.
+ */
+int mar_refresh_select(const float* partials, size_t partials_bytes,
+                       const int32_t* gp_idx, int ld_gp, int n_gp, int K,
+                       float* scores,
+                       int32_t* active_idx, int ld_act,
+                       int32_t* cached_idx, int ld_cached, int32_t* cached_len,
+                       int B, int H, int G, int N, void* stream);
 
 /*
  * mar_refresh_topk without a workspace argument, for callers that cannot

@@ -162,6 +162,27 @@ def test_topk_rejections(lib):
     assert topk(lib, ws_bytes=100) == E_WS
 
 
+def test_layer2_scores_and_select_rejections(lib):
+    f = lib.mar_cache_attn_fwd_scores
+    # q, k, v, out, lse, gen, ld_gen, G, partials, bytes, B, H, N, D, scale, dtype, stream
+    WS = 2 * 2 * 320 * 4
+    assert f(None, P, P, P, None, P, 16, 16, P, WS, 2, 2, 320, 64, 0.125, 1, None) == E_NULL
+    assert f(P, P, P, P, None, None, 16, 16, P, WS, 2, 2, 320, 64, 0.125, 1, None) == E_NULL
+    assert f(P, P, P, P, None, P, 8, 16, P, WS, 2, 2, 320, 64, 0.125, 1, None) == E_SHAPE   # ld_gen < G
+    assert f(P, P, P, P, None, P, 17, 17, P, WS, 2, 2, 320, 64, 0.125, 1, None) == E_UNSUP  # G > 16
+    assert f(P, P, P, P, None, P, 16, 16, P, WS, 2, 2, 384, 64, 0.125, 1, None) == E_UNSUP  # N > 320
+    assert f(P, P, P, P, None, P, 16, 16, P, WS, 2, 2, 64, 64, 0.125, 1, None) == E_UNSUP   # N <= 64
+    assert f(P, P, P, P, None, P, 16, 16, P, WS, 2, 2, 320, 64, 0.125, 0, None) == E_UNSUP  # fp32
+    assert f(P, P, P, P, None, P, 16, 16, P, WS - 4, 2, 2, 320, 64, 0.125, 1, None) == E_WS
+    g = lib.mar_refresh_select
+    # part, bytes, gp, ld_gp, n_gp, K, scores, act, ld_act, cached, ld_cached, len, B, H, G, N, s
+    assert g(None, WS, P, 32, 32, 16, P, P, 48, P, 320, P, 2, 2, 16, 320, None) == E_NULL
+    assert g(P, WS, P, 32, 32, 300, P, P, 332, P, 320, P, 2, 2, 16, 320, None) == E_RANGE
+    assert g(P, WS, P, 32, 32, 16, P, P, 40, P, 320, P, 2, 2, 16, 320, None) == E_SHAPE    # ld_act
+    assert g(P, WS - 4, P, 32, 32, 16, P, P, 48, P, 320, P, 2, 2, 16, 320, None) == E_WS
+    assert g(P, WS, P, 32, 32, 16, P, P, 48, P, 320, P, 2, 2, 0, 320, None) == E_SHAPE     # G < 1
+
+
 def test_refresh_topk_noalloc_rejections(lib):
     f = lib.mar_refresh_topk_noalloc
     # q, k, gp, ld_gp, n_gp, K, scale, scores, act, ld_act, cached, ld_cached, len, B, H, G, N, D, dt, s
