@@ -355,8 +355,11 @@ def other_configs(marca, dev, stream):
 
     from mar_workloads import CONFIGS, attention_inputs
     res = {}
-    for name, n_layers in (("mar_b", 12), ("mar_h", 4), ("highres", 4)):
-        cfg = CONFIGS[name]
+    for name, n_layers in (("mar_b", 12), ("mar_h", 4), ("highres", 4), ("mar_l_f32", 4)):
+        if name == "mar_l_f32":  # the MAR-L shape with fp32 inputs (the per-unit vector path)
+            cfg = CONFIGS["mar_l"].__class__(**{**CONFIGS["mar_l"].__dict__, "dtype": "f32"})
+        else:
+            cfg = CONFIGS[name]
         layers = []
         for l in range(n_layers):
             x = attention_inputs(cfg, dev, seed=cfg.seed * 100 + 50 + l)
@@ -385,7 +388,7 @@ def other_configs(marca, dev, stream):
         us = timed(lambda L: marca.mar_cache_attn_fwd(L["q_a"], L["k_a"], L["v_a"], L["k_cache"],
                                                       L["v_cache"], L["cached"], Nc=cfg.Nc,
                                                       out=L["out"]))
-        nbytes = attn_bytes(cfg.B, cfg.H, cfg.A, cfg.Nc, cfg.D)
+        nbytes = attn_bytes(cfg.B, cfg.H, cfg.A, cfg.Nc, cfg.D, 4 if cfg.dtype == "f32" else 2)
         gbs = nbytes / (us * 1e-6) / 1e9
         entry = {"sequences": cfg.B, "heads": cfg.H, "tokens": cfg.N, "active": cfg.A,
                  "cached": cfg.Nc, "attn_us_per_call": us, "attn_gbs": gbs,

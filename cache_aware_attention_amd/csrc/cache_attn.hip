@@ -28,8 +28,8 @@
 //    layers), 2 or 4 waves x 64 queries with them (also with per-sequence
 //    counts); the same MFMA tiles, with the softmax reference kept in scaled
 //    units and the query tiles in pairs.
-//  * attn_rowwise_kernel (fp32 any A, bf16 A < 16): one wave per query, one
-//    lane per head-dim element; plain FMA.  Exact-precision path for fp32.
+//  * attn_unit_kernel (fp32 any A, bf16 A < 16): a workgroup per unit and
+//    block of 64 queries streams 64-row K/V chunks through LDS; fp32 FMAs.
 //
 // Head dim is fixed at 64 (MAR-B/L/H all use 64).  The cached index list is
 // sanitised: an entry outside [0, N) is skipped, never dereferenced.  Inputs
@@ -48,104 +48,185 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
-// Row-wise path
+// Per-unit vector path (fp32 inputs at any A; bf16 below 16 active queries,
+// where a 16-wide MFMA tile would be mostly empty): fp32 FMAs throughout.
+//
+// A workgroup of 4 waves per (sequence, head) unit and block of 64 queries
+// streams the unit's virtual sequence [active rows ; cached rows] in chunks
+// of 64 rows through LDS, so every K/V row is read from memory once per
+// block.  Wave w holds queries 16w .. 16w+15 of the block: lane (kg, qi)
+// keeps query qi's 64 scaled elements in registers and scores keys kg + 4i
+// (i < 16) of the chunk against the K tile; the chunk's maximum, the
+// rescale of the running (max, sum, weighted sum) state -- the merge of the
+// two partial softmax sums, applied chunk by chunk across the active/cached
+// boundary -- and the probabilities follow; the probabilities go through an
+// LDS tile so that lane (kg, qi) can accumulate the weighted sum of V over
+// all 64 keys for head dims 16kg .. 16kg+15.  LDS rows are padded to 68
+// floats (rows four banks apart), so the reads are conflict-free.  A cached
+// entry outside [0, N) and rows past the sequence are masked, never read.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void load8(const float* p, int c, float (&x)[8]) {
-    const float4 a = reinterpret_cast<const float4*>(p)[2 * c];
-    const float4 b = reinterpret_cast<const float4*>(p)[2 * c + 1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-__device__ __forceinline__ void load8(const uint16_t* p, int c, float (&x)[8]) {
-    const uint4 a = reinterpret_cast<const uint4*>(p)[c];
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+constexpr int kUnitQ = 64;      // queries per workgroup
+constexpr int kUnitChunk = 64;  // key rows per chunk
+constexpr int kRowPad = 68;     // floats per LDS row
+constexpr int kPPad = 65;       // floats per query row of the probability tile
+
+__device__ __forceinline__ void load16(const float* p, float (&x)[16]) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        x[2 * k] = __uint_as_float(w[k] << 16);
-        x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    for (int c = 0; c < 4; ++c) {
+        const float4 a = reinterpret_cast<const float4*>(p)[c];
+        x[4 * c] = a.x; x[4 * c + 1] = a.y; x[4 * c + 2] = a.z; x[4 * c + 3] = a.w;
     }
 }
-__device__ __forceinline__ float load1(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ float load1(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ void load16(const uint16_t* p, float (&x)[16]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const uint4 a = reinterpret_cast<const uint4*>(p)[c];
+        const uint32_t wv[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[8 * c + 2 * k] = __uint_as_float(wv[k] << 16);
+            x[8 * c + 2 * k + 1] = __uint_as_float(wv[k] & 0xffff0000u);
+        }
+    }
+}
 __device__ __forceinline__ void store1(float* p, size_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void store1(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 
 template <typename T>
-__global__ __launch_bounds__(256) void attn_rowwise_kernel(
+__global__ __launch_bounds__(256) void attn_unit_kernel(
     const T* __restrict__ q_a, const T* __restrict__ k_a, const T* __restrict__ v_a,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ cached_idx, int ldc, T* __restrict__ out,
     float* __restrict__ lse, int H, int N, int A, int Nc, float scale_log2,
     const int32_t* __restrict__ a_len, const int32_t* __restrict__ c_len) {
-    __shared__ float q_s[4][kD];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x / kWave;
-    const int u = blockIdx.x;  // (b, h) unit
+    __shared__ __align__(16) float ks[kUnitChunk * kRowPad];
+    __shared__ __align__(16) float vs[kUnitChunk * kRowPad];
+    __shared__ float ps[4][16 * kPPad];
+    __shared__ int rowok_s[kUnitChunk];
+    const int tid = threadIdx.x;
+    const int w = tid / kWave, lane = tid & (kWave - 1);
+    const int qi = lane & 15, kg = lane >> 4;
+    const int u = blockIdx.x;
     const int b = u / H;
-    const int i = blockIdx.y * 4 + wid;  // query of this wave
-    // A and Nc are the row strides / list capacities; per-sequence counts may be smaller.
+    // A and Nc are the row stride / list capacity; per-sequence counts may be smaller.
     const int An = (a_len != nullptr) ? min(max(a_len[b], 0), A) : A;
     const int Ncn = (c_len != nullptr) ? min(max(c_len[b], 0), Nc) : Nc;
-    const bool has_query = i < An;
-    q_s[wid][lane] = has_query ? load1(q_a, ((size_t)u * A + i) * kD + lane) * scale_log2
-                               : 0.f;
-    __syncthreads();
-    if (!has_query) return;  // no block-wide barrier after this point
+    if (static_cast<int>(blockIdx.y) * kUnitQ >= An) return;  // uniform, before any barrier
+    const int q = blockIdx.y * kUnitQ + 16 * w + qi;             // this lane's query
+    const bool has_q = q < An;
 
-    const int n_rows = An + Ncn;
-    const int32_t* cidx = cached_idx + (size_t)b * ldc;
-    float m = -INFINITY, l = 0.f, o = 0.f;
-    for (int r0 = 0; r0 < n_rows; r0 += kWave) {
-        const int r = r0 + lane;
-        long long off_k = -1, off_v = -1;
-        if (r < An) {
-            off_k = ((long long)u * A + r) * kD;
-            off_v = off_k;
-        } else if (r < n_rows) {
-            const int n = cidx[r - An];
-            if (n >= 0 && n < N) {
-                off_k = ((long long)u * N + n) * kD + (1ll << 62);  // tag: cache source
-                off_v = off_k;
-            }
+    float qr[64];
+    {
+        const T* qp = q_a + (static_cast<size_t>(u) * A + min(q, An - 1)) * kD;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float x[16];
+            load16(qp + 16 * c, x);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) qr[16 * c + e] = x[e] * scale_log2;
         }
-        const bool valid = off_k >= 0;
-        float s = -INFINITY;
-        if (valid) {
-            const bool from_cache = off_k >= (1ll << 62);
-            const T* krow = from_cache ? k_cache + (off_k - (1ll << 62)) : k_a + off_k;
+    }
+    float m = -INFINITY, l = 0.f, o[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) o[d] = 0.f;
+
+    const int32_t* cidx = cached_idx + static_cast<size_t>(b) * ldc;
+    const int T_rows = An + Ncn;
+    const int lrow = tid >> 2, lq = tid & 3;  // loading thread: row, quarter of the row
+    for (int r0 = 0; r0 < T_rows; r0 += kUnitChunk) {
+        // Load the chunk's K and V rows (a thread: 16 elements of one row).
+        {
+            const int r = r0 + lrow;
+            const T* kp = nullptr;
+            const T* vp = nullptr;
+            if (r < An) {
+                kp = k_a + (static_cast<size_t>(u) * A + r) * kD;
+                vp = v_a + (static_cast<size_t>(u) * A + r) * kD;
+            } else if (r < T_rows) {
+                const int n = cidx[r - An];
+                if (n >= 0 && n < N) {
+                    kp = k_cache + (static_cast<size_t>(u) * N + n) * kD;
+                    vp = v_cache + (static_cast<size_t>(u) * N + n) * kD;
+                }
+            }
+            float kx[16], vx[16];
+            if (kp != nullptr) {
+                load16(kp + 16 * lq, kx);
+                load16(vp + 16 * lq, vx);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) kx[e] = vx[e] = 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                *reinterpret_cast<float4*>(ks + lrow * kRowPad + 16 * lq + 4 * c) =
+                    make_float4(kx[4 * c], kx[4 * c + 1], kx[4 * c + 2], kx[4 * c + 3]);
+                *reinterpret_cast<float4*>(vs + lrow * kRowPad + 16 * lq + 4 * c) =
+                    make_float4(vx[4 * c], vx[4 * c + 1], vx[4 * c + 2], vx[4 * c + 3]);
+            }
+            if (lq == 0) rowok_s[lrow] = (kp != nullptr) ? 1 : 0;
+        }
+        __syncthreads();
+        // Scores of query qi against keys kg + 4i of the chunk.
+        float sc[16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = kg + 4 * i;
+            const float* kr = ks + j * kRowPad;
             float acc = 0.f;
 #pragma unroll
-            for (int c = 0; c < kD / 8; ++c) {
-                float x[8];
-                load8(krow, c, x);
+            for (int c = 0; c < 16; ++c) {
+                const float4 k4 = *reinterpret_cast<const float4*>(kr + 4 * c);
+                acc = fmaf(qr[4 * c], k4.x, acc);
+                acc = fmaf(qr[4 * c + 1], k4.y, acc);
+                acc = fmaf(qr[4 * c + 2], k4.z, acc);
+                acc = fmaf(qr[4 * c + 3], k4.w, acc);
+            }
+            sc[i] = rowok_s[j] ? acc : -INFINITY;
+            mx = fmaxf(mx, sc[i]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float mn = fmaxf(m, mx);
+        const float mu = (mn == -INFINITY) ? 0.f : mn;  // no valid key yet: every term is 0
+        const float alpha = exp2f(m - mu);
+        float psum = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(q_s[wid][8 * c + e], x[e], acc);
-            }
-            s = acc;
+        for (int i = 0; i < 16; ++i) {
+            const float pv = exp2f(sc[i] - mu);
+            ps[w][qi * kPPad + kg + 4 * i] = pv;
+            psum += pv;
         }
-        const float mc = wave_max(s);
-        const float mn = fmaxf(m, mc);
-        if (mn == -INFINITY) continue;  // wave-uniform: nothing valid yet
-        const float alpha = exp2f(m - mn);
-        const float p = valid ? exp2f(s - mn) : 0.f;
-        l = l * alpha + wave_sum(p);
-        o *= alpha;
-        const int cnt = min(kWave, n_rows - r0);
-        for (int j = 0; j < cnt; ++j) {
-            const float pj = __shfl(p, j, kWave);
-            const long long ov = __shfl(off_v, j, kWave);
-            if (pj != 0.f) {
-                const bool from_cache = ov >= (1ll << 62);
-                const T* vrow = from_cache ? v_cache + (ov - (1ll << 62)) : v_a + ov;
-                o = fmaf(pj, load1(vrow, lane), o);
-            }
-        }
+        psum += __shfl_xor(psum, 16, kWave);
+        psum += __shfl_xor(psum, 32, kWave);
+        l = l * alpha + psum;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) o[d] *= alpha;
         m = mn;
+        __syncthreads();  // the probability tile is complete
+        // o[d] += sum over the chunk's keys j of p(qi, j) * V[j][16kg + d]
+        for (int j = 0; j < kUnitChunk; ++j) {
+            const float pj = ps[w][qi * kPPad + j];
+            const float* vr = vs + j * kRowPad + 16 * kg;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float4 v4 = *reinterpret_cast<const float4*>(vr + 4 * c);
+                o[4 * c] = fmaf(pj, v4.x, o[4 * c]);
+                o[4 * c + 1] = fmaf(pj, v4.y, o[4 * c + 1]);
+                o[4 * c + 2] = fmaf(pj, v4.z, o[4 * c + 2]);
+                o[4 * c + 3] = fmaf(pj, v4.w, o[4 * c + 3]);
+            }
+        }
+        __syncthreads();  // every wave is done with the tiles
     }
-    const size_t orow = ((size_t)u * A + i) * kD;
-    store1(out, orow + lane, l > 0.f ? o / l : 0.f);
-    if (lse != nullptr && lane == 0) lse[(size_t)u * A + i] = (l > 0.f) ? (m + log2f(l)) * kLn2
-                                                                        : -INFINITY;
+    if (!has_q) return;
+    const size_t orow = (static_cast<size_t>(u) * A + q) * kD + 16 * kg;
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) store1(out, orow + d, o[d] * inv);
+    if (lse != nullptr && kg == 0)
+        lse[static_cast<size_t>(u) * A + q] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -1612,16 +1693,16 @@ int launch_attn_impl(const void* q_a, const void* k_a, const void* v_a, const vo
         return dispatch_mfma<false>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A, Nc,
                                     scale_log2, nullptr, 0, nullptr, a_len, c_len, stream);
     }
-    const dim3 grid(B * H, (A + 3) / 4);
+    const dim3 grid(B * H, (A + kUnitQ - 1) / kUnitQ);
     if (dtype == MAR_BF16) {
-        hipLaunchKernelGGL(attn_rowwise_kernel<uint16_t>, grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL(attn_unit_kernel<uint16_t>, grid, dim3(256), 0, stream,
                            static_cast<const uint16_t*>(q_a), static_cast<const uint16_t*>(k_a),
                            static_cast<const uint16_t*>(v_a), static_cast<const uint16_t*>(k_cache),
                            static_cast<const uint16_t*>(v_cache), cached_idx, ldc,
                            static_cast<uint16_t*>(out), lse, H, N, A, Nc, scale_log2, a_len,
                            c_len);
     } else {
-        hipLaunchKernelGGL(attn_rowwise_kernel<float>, grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL(attn_unit_kernel<float>, grid, dim3(256), 0, stream,
                            static_cast<const float*>(q_a), static_cast<const float*>(k_a),
                            static_cast<const float*>(v_a), static_cast<const float*>(k_cache),
                            static_cast<const float*>(v_cache), cached_idx, ldc,
