@@ -355,7 +355,7 @@ def other_configs(marca, dev, stream):
 
     from mar_workloads import CONFIGS, attention_inputs
     res = {}
-    for name, n_layers in (("mar_b", 12), ("mar_h", 4), ("highres", 4), ("mar_l_f32", 4)):
+    for name, n_layers in (("mar_b", 12), ("mar_h", 4), ("highres", 6), ("mar_l_f32", 4)):
         if name == "mar_l_f32":  # the MAR-L shape with fp32 inputs (the per-unit vector path)
             cfg = CONFIGS["mar_l"].__class__(**{**CONFIGS["mar_l"].__dict__, "dtype": "f32"})
         else:
@@ -397,16 +397,19 @@ def other_configs(marca, dev, stream):
         if name == "highres":
             full = torch.empty_like(layers[0]["k_cache"])
             flops = 4 * cfg.B * cfg.H * cfg.N * cfg.N * cfg.D
-            f_us = timed(lambda L: marca.mar_cache_attn_fwd(L["k_cache"], L["k_cache"], L["v_cache"],
+            # the queries: the K of the layer three away (no tensor is read
+            # twice in a call or by two consecutive calls)
+            qof = {id(L): layers[(i + 3) % len(layers)]["k_cache"] for i, L in enumerate(layers)}
+            f_us = timed(lambda L: marca.mar_cache_attn_fwd(qof[id(L)], L["k_cache"], L["v_cache"],
                                                             L["k_cache"], L["v_cache"], None, Nc=0,
                                                             out=full))
             entry["full_attn_us_per_call"] = f_us
             entry["full_attn_tflops"] = flops / f_us / 1e6
             entry["full_attn_roofline"] = roofline_for(flops, 4 * cfg.B * cfg.H * cfg.N * cfg.D * 2,
                                                        f_us * 1e-6)
-            # refresh step: each layer's caches take the next layer's rows as
-            # fresh K/V; the queries come from the layer after that
-            nxt = {id(L): (layers[(i + 1) % len(layers)], layers[(i + 2) % len(layers)])
+            # refresh step: each layer's caches take the rows of the layer two
+            # away as fresh K/V; the queries come from the layer four away
+            nxt = {id(L): (layers[(i + 2) % len(layers)], layers[(i + 4) % len(layers)])
                    for i, L in enumerate(layers)}
             # the token gate at this shape (W = 1024, C5's gated layers)
             from mar_workloads import device_gate_features
@@ -491,12 +494,13 @@ def main():
           flush=True)
     x = build_inputs(cfg, dev)
     # layer 2 in two passes needs the generating rows of each layer's queries
-    # (layer l + 1's K stands in for layer l's queries) as their own tensor
+    # (the K of the layer half the stack away stands in for layer l's
+    # queries, as in full_attn below) as their own tensor
     n_layers = cfg.layers - 2
     gen_pos = x["gp"][:, cfg.n_prev:cfg.n_prev + cfg.n_gen].long()
     gidx = gen_pos[:, None, :, None].expand(cfg.B, cfg.H, cfg.n_gen, cfg.D)
     for l in range(n_layers):
-        Lq = x["layers"][(l + 1) % n_layers]["k_cache"]
+        Lq = x["layers"][(l + n_layers // 2) % n_layers]["k_cache"]
         x["layers"][l]["q_gen2"] = torch.gather(Lq, 2, gidx).contiguous()
     torch.cuda.synchronize()
     counts = [cfg.n_gen] * (cfg.steps)
@@ -576,9 +580,12 @@ def main():
     def full_attn(l):
         """A full-attention layer (layers 1-2 of every step, every layer of a
         refresh step): all N tokens active, no cached rows.  Layer l's stored
-        K/V stand in for its fresh K/V and the next layer's K for its Q."""
+        K/V stand in for its fresh K/V and the K of the layer half the stack
+        away for its Q, so that no tensor is read by two consecutive calls
+        (consecutive layers' working sets would otherwise share one in the
+        last-level cache)."""
         x = X[0]
-        L, Lq = x["layers"][l], x["layers"][(l + 1) % n_ca]
+        L, Lq = x["layers"][l], x["layers"][(l + n_ca // 2) % n_ca]
         prepared(("full", l), marca.mar_cache_attn_fwd, Lq["k_cache"], L["k_cache"], L["v_cache"],
                  L["k_cache"], L["v_cache"], None, Nc=0, out=x["full_out"], stream=stream)()
 
@@ -599,7 +606,7 @@ def main():
         that also writes the generating queries' per-head probability sums,
         then the selection from them."""
         x = X[0]
-        L, Lq = x["layers"][l], x["layers"][(l + 1) % n_ca]
+        L, Lq = x["layers"][l], x["layers"][(l + n_ca // 2) % n_ca]
         gen = x["gp"][:, plan.n_prev:plan.n_prev + plan.n_gen]
         prepared(("l2scores", l, plan.n_prev, plan.n_gen), marca.mar_cache_attn_fwd_scores,
                  Lq["k_cache"], L["k_cache"], L["v_cache"], gen, plan.n_gen,
@@ -650,10 +657,11 @@ def main():
     def full_refresh(l):
         """A refresh step of cache-aware layer l: full attention over all N tokens
         and the rewrite of every row of the layer's cache with the fresh K/V, in
-        one call (the next layer's stored K/V stand in for the fresh K/V, the one
-        after it for Q)."""
+        one call (the stored K/V of the layer a third of the stack away stand in
+        for the fresh K/V, the K of the layer two thirds away for Q: no tensor
+        is read by two consecutive calls)."""
         x = X[0]
-        L, Ln, Lq = (x["layers"][(l + i) % n_ca] for i in range(3))
+        L, Ln, Lq = (x["layers"][(l + i * (n_ca // 3)) % n_ca] for i in range(3))
         prepared(("refresh", l), marca.mar_cache_attn_fwd_update, Lq["k_cache"], Ln["k_cache"],
                  Ln["v_cache"], L["k_cache"], L["v_cache"], None, None, Nc=0, out=x["full_out"],
                  stream=stream)()

@@ -3,6 +3,8 @@
 // the whole-row / MFMA-operand exchange).  gfx950 only.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <cstdint>
 
 #include "mar_cache_attn.h"
@@ -90,6 +92,28 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 
 inline int status_from_launch() {
     return hipGetLastError() == hipSuccess ? MAR_OK : MAR_E_LAUNCH;
+}
+
+// The number of compute units of the device `stream` runs on (the current
+// device for the null stream), asked once per device and kept.
+inline int compute_units(hipStream_t stream, int* cus) {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> known[kMaxDev];
+    int dev = 0;
+    if ((stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess) {
+        (void)hipGetLastError();
+        return MAR_E_LAUNCH;
+    }
+    int n = (dev >= 0 && dev < kMaxDev) ? known[dev].load(std::memory_order_relaxed) : 0;
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            return MAR_E_LAUNCH;
+        }
+        if (dev >= 0 && dev < kMaxDev) known[dev].store(n, std::memory_order_relaxed);
+    }
+    *cus = n;
+    return MAR_OK;
 }
 
 // Streaming 16-byte load (nontemporal: the line is not kept for reuse).  On

@@ -240,6 +240,39 @@ def test_full_attention_full_size(marca, name, update):
         check(np64(out[b, h])[None], np64(lse[b, h])[None], o[0], l[0], "bf16")
 
 
+@pytest.mark.parametrize("B,H,N,update", [(64, 20, 200, False), (64, 20, 200, True),
+                                          (16, 40, 650, False), (16, 40, 650, True)])
+def test_full_attention_several_items_per_workgroup(marca, B, H, N, update):
+    """More (unit, query block) items than resident workgroups, so each
+    workgroup carries its chunk stream and its prefetched queries from one
+    item to the next: an odd number of chunks per unit (the LDS buffer of an
+    item's first chunk alternates), and with N = 650 three blocks per unit and
+    a partial last chunk.  With the update the caches must come out equal to
+    the fresh K/V."""
+    from mar_workloads import device_normal
+    import oracle
+    q, k, v = (device_normal((B, H, N, 64), 900 + N + i, DEV, torch.bfloat16) for i in range(3))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    if update:
+        kc, vc = torch.zeros_like(k), torch.zeros_like(v)
+        out = marca.mar_cache_attn_fwd_update(q, k, v, kc, vc, None, None, Nc=0, lse=lse)
+    else:
+        out = marca.mar_cache_attn_fwd(q, k, v, k, v, None, Nc=0, lse=lse)
+    torch.cuda.synchronize()
+    if update:
+        assert torch.equal(kc, k) and torch.equal(vc, v)
+        del kc, vc
+    rng = np.random.default_rng(N + update)
+    units = [(0, 0), (B - 1, H - 1)] + [(int(rng.integers(B)), int(rng.integers(H)))
+                                        for _ in range(4)]
+    for b, h in units:
+        sl = lambda t: np64(t[b:b + 1, h:h + 1])
+        o, l = oracle.cache_attention(sl(q), sl(k), sl(v), sl(k), sl(v),
+                                      np.zeros((1, 1), np.int32), 0.125, Nc=0)
+        check(np64(out[b, h])[None], np64(lse[b, h])[None], o[0], l[0], "bf16")
+    assert torch.isfinite(out.float()).all()
+
+
 @pytest.mark.parametrize("name", ["mar_b", "mar_l", "mar_h", "highres"])
 def test_full_size_sampled_units(marca, name):
     """Full-size MAR shapes, the launch configuration the benchmark times;
