@@ -429,6 +429,195 @@ def other_configs(marca, dev, stream):
     return res
 
 
+C5_ROUNDS = 3
+
+
+def c5_decode(marca, dev, stream, rounds=C5_ROUNDS):
+    """The high-res configuration's whole 64-step decode of the attention path
+    at full size: 64 sequences (32 images x 2 CFG), 16 heads, 1088 tokens (64
+    prefix + 1024 image), 32 layers, active budget 128, a refresh every third
+    step, and LazyMAR's token gate on layers 4-32 (1024-wide features,
+    threshold 0.95, seeded 84% reuse).  A cached step runs: layer 1 full
+    attention; layer 2 full attention, then the refresh scores + top-K over
+    the same K (mar_refresh_topk: 1088 tokens is past the single-pass scores
+    kernel);
+    layer 3 the fused cache-aware attention + cache update of its 128 active
+    rows; layers 4-32 the gate (which also lists each sequence's reused
+    positions), the ragged attention of each sequence's recomputed tokens
+    over their fresh K/V and the cached K/V of its reused tokens, and the
+    scatter of the recomputed rows into the layer's cache; the CFG residual
+    reuse.  A refresh step runs full attention in every layer, layers 3-32
+    rewriting their caches in the same call, and stores the CFG residual.
+    Modes as for MAR-L: no caches (full attention everywhere), the caches,
+    and the caches + condition cache (the steps between refreshes compute the
+    conditional half of the batch only).  Every layer has its own caches,
+    gate features and recomputed-row Q/K/V; the fresh Q/K/V of a
+    full-attention call are other layers' caches a third and two thirds of
+    the stack away, so no tensor is read by two consecutive calls.  The gate
+    features do not change between steps (their upkeep is the model's), so
+    each layer recomputes the same tokens at every step."""
+    import torch
+
+    from mar_workloads import (CONFIGS, cfg_outputs, cosine_counts, device_gate_features,
+                               device_normal, generation_order)
+    cfg = CONFIGS["highres"]
+    B, H, N, D, L = cfg.B, cfg.H, cfg.N, cfg.D, cfg.layers
+    n_ca = L - 2                   # cache-aware layers 3..32 (index 0 is layer 3)
+    n_gated = n_ca - 1             # layers 4..32 (index 1..)
+    bf = torch.bfloat16
+    t_setup = time.perf_counter()
+    kc = [device_normal((B, H, N, D), 8000 + 2 * i, dev, bf) for i in range(n_ca)]
+    vc = [device_normal((B, H, N, D), 8001 + 2 * i, dev, bf) for i in range(n_ca)]
+    counts = cosine_counts(cfg.n_img, cfg.steps)
+    plans = [marca.mar_plan_step(counts, t, N, cfg.budget) for t in range(cfg.steps)]
+    order = torch.from_numpy(generation_order(cfg)).to(dev)
+    # per step: the G then P list of the top-K and the generating queries of layer 2
+    gp = {}
+    qgen = {}
+    for t, p in enumerate(plans):
+        if p.refresh:
+            continue
+        gp[t] = order[:, p.prev_begin:p.gen_begin + p.n_gen].contiguous()
+        if p.n_gen not in qgen:
+            qgen[p.n_gen] = device_normal((B, H, p.n_gen, D), 8900 + p.n_gen, dev, bf)
+    A3 = cfg.budget
+    q3, k3, v3 = (device_normal((B, H, A3, D), 8800 + i, dev, bf) for i in range(3))
+    ws = torch.empty((marca.mar_refresh_topk_workspace(B, H, N) // 4,), dtype=torch.float32,
+                     device=dev)
+    sel = {"scores": torch.empty((B, N), dtype=torch.float32, device=dev),
+           "active": torch.empty((B, A3), dtype=torch.int32, device=dev),
+           "cached": torch.empty((B, N - A3), dtype=torch.int32, device=dev),
+           "clen": torch.empty((B,), dtype=torch.int32, device=dev)}
+    gate_out = {"cos": torch.empty((B, N), dtype=torch.float32, device=dev),
+                "reuse": torch.empty((B, N), dtype=torch.uint8, device=dev),
+                "cidx": torch.empty((B, N), dtype=torch.int32, device=dev),
+                "clen": torch.empty((B,), dtype=torch.int32, device=dev),
+                "ridx": torch.empty((B, N), dtype=torch.int32, device=dev),
+                "rlen": torch.empty((B,), dtype=torch.int32, device=dev)}
+    gx, gy, qc, kcn, vcn, acap = [None], [None], [None], [None], [None], [0]
+    for i in range(1, n_ca):
+        x_cur, x_cached, _ = device_gate_features(B, N, cfg.W, seed=cfg.seed + 17 * i, device=dev)
+        gx.append(x_cur)
+        gy.append(x_cached)
+        marca.mar_cos_gate(x_cur, x_cached, cfg.tau, compute_len=gate_out["clen"])
+        cap = int(gate_out["clen"].max())  # the recomputed rows' capacity (same every step)
+        acap.append(cap)
+        qc.append(device_normal((B, H, cap, D), 9000 + 3 * i, dev, bf))
+        kcn.append(device_normal((B, H, cap, D), 9001 + 3 * i, dev, bf))
+        vcn.append(device_normal((B, H, cap, D), 9002 + 3 * i, dev, bf))
+    c0, u0, c1, _ = cfg_outputs(cfg.B_img, cfg.n_img, 16, seed=cfg.seed)
+    cond = torch.from_numpy(c1).to(dev)
+    uncond = torch.from_numpy(u0).to(dev)
+    residual = torch.from_numpy(c0 - u0).to(dev)
+    uncond_out = torch.empty_like(cond)
+    full_out = torch.empty((B, H, N, D), dtype=bf, device=dev)
+    out3 = torch.empty((B, H, A3, D), dtype=bf, device=dev)
+    outc = [None] + [torch.empty_like(qc[i]) for i in range(1, n_ca)]
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    P = marca.prepare
+    prep = {}
+    half = [B]
+
+    def run(key, fn, *a, **kw):
+        """fn(*a, **kw) marshalled once per (batch size, key), then replayed."""
+        k = (half[0],) + key
+        if k not in prep:
+            nb = half[0]
+            a = [t[:nb] if isinstance(t, torch.Tensor) and t.shape[0] == B else t for t in a]
+            kw = {n: (t[:nb] if isinstance(t, torch.Tensor) and t.shape[0] == B else t)
+                  for n, t in kw.items()}
+            prep[k] = P(fn, *a, **kw)
+        prep[k]()
+
+    third = n_ca // 3
+
+    def full(l):  # full attention of layer l (0..31): K/V of cache l mod 30, Q two thirds away
+        i = l % n_ca
+        run(("full", l), marca.mar_cache_attn_fwd, kc[(i + 2 * third) % n_ca], kc[i], vc[i],
+            kc[i], vc[i], None, Nc=0, out=full_out, stream=stream)
+
+    def refresh(i):  # cache-aware layer i on a refresh step: fresh K/V a third away
+        j, k = (i + third) % n_ca, (i + 2 * third) % n_ca
+        run(("refresh", i), marca.mar_cache_attn_fwd_update, kc[k], kc[j], vc[j], kc[i], vc[i],
+            None, None, Nc=0, out=full_out, stream=stream)
+
+    def cached_step(t):
+        p = plans[t]
+        full(0)
+        full(1)
+        run(("topk", t), marca.mar_refresh_topk, qgen[p.n_gen], kc[1], gp[t],
+            p.n_prev + p.n_gen, p.n_refresh, scores=sel["scores"], active_idx=sel["active"],
+            cached_idx=sel["cached"], cached_len=sel["clen"], workspace=ws, stream=stream)
+        run(("fused",), marca.mar_cache_attn_fwd_update, q3, k3, v3, kc[0], vc[0], sel["cached"],
+            sel["active"], Nc=N - A3, out=out3, stream=stream)
+        for i in range(1, n_ca):
+            run(("gate", i), marca.mar_cos_gate, gx[i], gy[i], cfg.tau, cos_out=gate_out["cos"],
+                reuse_mask=gate_out["reuse"], compute_idx=gate_out["cidx"],
+                compute_len=gate_out["clen"], reuse_idx=gate_out["ridx"],
+                reuse_len=gate_out["rlen"], stream=stream)
+            run(("ragged", i), marca.mar_cache_attn_fwd_ragged, qc[i], kcn[i], vcn[i], kc[i],
+                vc[i], gate_out["ridx"], gate_out["clen"], gate_out["rlen"], out=outc[i],
+                stream=stream)
+            run(("scatter", i), marca.mar_kv_scatter_refresh, kc[i], vc[i], kcn[i], vcn[i],
+                gate_out["cidx"], stream=stream)
+        run(("cfg_reuse",), marca.mar_cfg_residual, cond, residual=residual,
+            mode=marca.MAR_CFG_REUSE, uncond_out=uncond_out, stream=stream)
+
+    def decode(mode):
+        for t, p in enumerate(plans):
+            if mode == "none":
+                for l in range(L):
+                    full(l)
+                continue
+            if p.refresh:
+                full(0)
+                full(1)
+                for i in range(n_ca):
+                    refresh(i)
+                run(("cfg_store",), marca.mar_cfg_residual, cond, uncond, residual=residual,
+                    mode=marca.MAR_CFG_STORE, stream=stream)
+                continue
+            if mode == "cache+cond":
+                half[0] = B // 2
+            cached_step(t)
+            half[0] = B
+
+    modes = ("cache", "none", "cache+cond")
+    samples = {m: [] for m in modes}
+    for m in modes:
+        decode(m)
+    torch.cuda.synchronize()
+    for r in range(rounds):
+        for j in range(len(modes)):
+            m = modes[(j + r) % len(modes)]
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            decode(m)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            samples[m].append(e0.elapsed_time(e1))
+    med = {m: sorted(v)[len(v) // 2] for m, v in samples.items()}
+    res = {
+        "what": " ".join(c5_decode.__doc__.split()),
+        "sequences": B, "heads": H, "tokens": N, "layers": L, "budget": cfg.budget,
+        "gate_width": cfg.W, "gated_layers": n_gated, "steps": cfg.steps,
+        "refresh_steps": sum(p.refresh for p in plans),
+        "recomputed_rows_capacity": acap[1:],
+        "timing": f"median of {rounds} interleaved runs per mode",
+        "samples_ms": samples,
+        "ms": med["cache"], "ms_no_cache": med["none"], "ms_cond_cache": med["cache+cond"],
+        "speedup": med["none"] / med["cache"],
+        "speedup_cond_cache": med["none"] / med["cache+cond"],
+        "setup_s": setup_s,
+    }
+    del kc, vc, gx, gy, qc, kcn, vcn, prep
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -437,6 +626,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the whole-decode timing (for counter runs)")
+    ap.add_argument("--c5-only", action="store_true",
+                    help="only the full-size high-res 64-step decode (one JSON object)")
     ap.add_argument("--locality-only", action="store_true",
                     help="only the locality comparison's kernels, a fixed sequence (counter runs)")
     ap.add_argument("--copy-only", action="store_true",
@@ -456,6 +647,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = CONFIGS["mar_l"]
+
+    if args.c5_only:
+        print(json.dumps(c5_decode(marca, dev, torch.cuda.current_stream())))
+        return
 
     if args.locality_only:
         # Per split, in this order: 3 passes of the cache-aware attention over
@@ -842,6 +1037,9 @@ def main():
 
     configs = None if args.no_decode else other_configs(marca, dev, stream)
     loc = None if args.no_decode else locality(marca, dev, stream)
+    if not args.no_decode:
+        print("bench: high-res 64-step decode", file=sys.stderr, flush=True)
+    c5 = None if args.no_decode else c5_decode(marca, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -904,6 +1102,7 @@ def main():
             "separate_us": avg_us["layer2_separate"], "fused_us": avg_us["layer2_fused"],
             "saved_us": avg_us["layer2_separate"] - avg_us["layer2_fused"]},
         "locality": loc,
+        "c5_decode": c5,
         "attn_median_us": attn_median_us,
         "attn_frac_of_copy": (achieved / copy_gbs) if copy_gbs else None,
         "fused_frac_of_copy": (achieved_fused / copy_gbs) if copy_gbs else None,

@@ -82,7 +82,7 @@ def load_library(path: Optional[str] = None):
     lib.mar_refresh_topk_noalloc.argtypes = [V, V, V, I, I, I, F, V, V, I, V, I, V, I, I, I, I,
                                              I, I, V]
     lib.mar_cos_gate.restype = I
-    lib.mar_cos_gate.argtypes = [V, V, F, F, V, V, V, V, I, I, I, I, V]
+    lib.mar_cos_gate.argtypes = [V, V, F, F, V, V, V, V, V, V, I, I, I, I, V]
     lib.mar_cfg_residual.restype = I
     lib.mar_cfg_residual.argtypes = [V, V, V, V, V, F, I, ctypes.c_int64, V]
     lib.mar_plan_step.restype = I
@@ -446,8 +446,11 @@ def mar_refresh_topk_noalloc(q_gen, k_full, gp_idx, n_gp, K, scores=None, active
 
 
 def mar_cos_gate(x_cur, x_cached, tau=0.95, eps=1e-8, cos_out=None, reuse_mask=None,
-                 compute_idx=None, compute_len=None, stream=None):
-    """Returns (cos [B,N] f32, reuse [B,N] u8, compute_idx [B,N] i32, compute_len [B] i32)."""
+                 compute_idx=None, compute_len=None, reuse_idx=None, reuse_len=None,
+                 stream=None):
+    """Returns (cos [B,N] f32, reuse [B,N] u8, compute_idx [B,N] i32, compute_len [B] i32).
+    With reuse_idx [B,N] i32 and reuse_len [B] i32 given (both or neither),
+    also fills the ascending reusing positions (-1 padded) and their counts."""
     B, N, W = x_cur.shape
     code = _dtype_code(x_cur)
     _dev(x_cached, "x_cached", x_cur.dtype, (B, N, W))
@@ -465,7 +468,10 @@ def mar_cos_gate(x_cur, x_cached, tau=0.95, eps=1e-8, cos_out=None, reuse_mask=N
         _dev(cos_out, "cos_out", torch.float32, (B, N)),
         _dev(reuse_mask, "reuse_mask", torch.uint8, (B, N)),
         _dev(compute_idx, "compute_idx", torch.int32, (B, N)),
-        _dev(compute_len, "compute_len", torch.int32, (B,)), B, N, W, code, _stream(stream))
+        _dev(compute_len, "compute_len", torch.int32, (B,)),
+        None if reuse_idx is None else _dev(reuse_idx, "reuse_idx", torch.int32, (B, N)),
+        None if reuse_len is None else _dev(reuse_len, "reuse_len", torch.int32, (B,)),
+        B, N, W, code, _stream(stream))
     return cos_out, reuse_mask, compute_idx, compute_len
 
 

@@ -213,9 +213,11 @@ extern "C" int mar_refresh_topk_noalloc(const void* q_gen, const void* k_full,
 
 extern "C" int mar_cos_gate(const void* x_cur, const void* x_cached, float tau, float eps,
                             float* cos_out, uint8_t* reuse_mask, int32_t* compute_idx,
-                            int32_t* compute_len, int B, int N, int W, int dtype, void* stream) {
+                            int32_t* compute_len, int32_t* reuse_idx, int32_t* reuse_len, int B,
+                            int N, int W, int dtype, void* stream) {
     if (!x_cur || !x_cached || !cos_out || !reuse_mask || !compute_idx || !compute_len)
         return MAR_E_NULL;
+    if ((reuse_idx == nullptr) != (reuse_len == nullptr)) return MAR_E_NULL;
     const int eb = elem_bytes(dtype);
     if (eb == 0) return MAR_E_DTYPE;
     if (B < 1 || N < 1 || W < 1) return MAR_E_SHAPE;
@@ -223,7 +225,7 @@ extern "C" int mar_cos_gate(const void* x_cur, const void* x_cached, float tau, 
     if (!(tau == tau) || !(eps >= 0.f)) return MAR_E_RANGE;
     if (!aligned16(x_cur) || !aligned16(x_cached)) return MAR_E_RANGE;
     return marca::launch_cos_gate(x_cur, x_cached, tau, eps, cos_out, reuse_mask, compute_idx,
-                                  compute_len, B, N, W, dtype, stream);
+                                  compute_len, reuse_idx, reuse_len, B, N, W, dtype, stream);
 }
 
 extern "C" int mar_cfg_residual(const float* cond, const float* uncond, float* residual,

@@ -8,7 +8,9 @@
 // cos >= tau in float: several tokens per wave with all their loads in
 // flight for widths up to 256 pieces of 16 bytes, one token per wave above.
 // Kernel 2 (one workgroup per sequence) packs the positions to recompute in
-// ascending order with a block prefix sum.
+// ascending order with a block prefix sum, and optionally the positions that
+// reuse (every position before a thread's range that is not recomputed
+// reuses, so one scan places both lists).
 #include "device_util.h"
 #include "launch.h"
 
@@ -138,30 +140,44 @@ void launch_cosine_multi(const void* x, const void* y, float* cos_out, uint8_t* 
 __global__ __launch_bounds__(kThreads) void compact_kernel(const uint8_t* __restrict__ reuse,
                                                            int32_t* __restrict__ compute_idx,
                                                            int32_t* __restrict__ compute_len,
+                                                           int32_t* __restrict__ reuse_idx,
+                                                           int32_t* __restrict__ reuse_len,
                                                            int N) {
     __shared__ int scan_scratch[kThreads / kWave];
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
     const uint8_t* r = reuse + (size_t)b * N;
     const int per = (N + kThreads - 1) / kThreads;
-    const int j0 = tid * per;
+    const int j0 = min(N, tid * per);
     const int j1 = min(N, j0 + per);
     int cnt = 0;
     for (int j = j0; j < j1; ++j) cnt += (r[j] == 0);
     int total = 0;
     int pos = block_exclusive_scan<kThreads>(cnt, scan_scratch, &total);
+    int pos_r = j0 - pos;  // the reusing positions before j0
     int32_t* row = compute_idx + (size_t)b * N;
-    for (int j = j0; j < j1; ++j)
-        if (r[j] == 0) row[pos++] = j;
+    int32_t* rrow = reuse_idx != nullptr ? reuse_idx + (size_t)b * N : nullptr;
+    for (int j = j0; j < j1; ++j) {
+        if (r[j] == 0)
+            row[pos++] = j;
+        else if (rrow != nullptr)
+            rrow[pos_r++] = j;
+    }
     for (int t = total + tid; t < N; t += kThreads) row[t] = -1;
-    if (tid == 0) compute_len[b] = total;
+    if (rrow != nullptr)
+        for (int t = N - total + tid; t < N; t += kThreads) rrow[t] = -1;
+    if (tid == 0) {
+        compute_len[b] = total;
+        if (reuse_len != nullptr) reuse_len[b] = N - total;
+    }
 }
 
 }  // namespace
 
 int launch_cos_gate(const void* x_cur, const void* x_cached, float tau, float eps,
                     float* cos_out, uint8_t* reuse_mask, int32_t* compute_idx,
-                    int32_t* compute_len, int B, int N, int W, int dtype, void* stream_v) {
+                    int32_t* compute_len, int32_t* reuse_idx, int32_t* reuse_len, int B, int N,
+                    int W, int dtype, void* stream_v) {
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
     const long long tokens = (long long)B * N;
     const int waves_per_block = kThreads / kWave;
@@ -187,7 +203,7 @@ int launch_cos_gate(const void* x_cur, const void* x_cached, float tau, float ep
     int st = status_from_launch();
     if (st != MAR_OK) return st;
     hipLaunchKernelGGL(compact_kernel, dim3(B), dim3(kThreads), 0, stream, reuse_mask, compute_idx,
-                       compute_len, N);
+                       compute_len, reuse_idx, reuse_len, N);
     return status_from_launch();
 }
 

@@ -63,7 +63,8 @@ int launch_refresh_topk_noalloc(const void* q_gen, const void* k_full,
 
 int launch_cos_gate(const void* x_cur, const void* x_cached, float tau, float eps,
                     float* cos_out, uint8_t* reuse_mask, int32_t* compute_idx,
-                    int32_t* compute_len, int B, int N, int W, int dtype, void* stream);
+                    int32_t* compute_len, int32_t* reuse_idx, int32_t* reuse_len, int B, int N,
+                    int W, int dtype, void* stream);
 
 int launch_cfg_residual(const float* cond, const float* uncond, float* residual,
                         float* uncond_out, float* guided_out, float cfg_scale, int mode,

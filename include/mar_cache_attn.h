@@ -302,11 +302,17 @@ int mar_refresh_topk_noalloc(const void* q_gen, const void* k_full,
  *   reuse_mask  [B,N] uint8   1 iff cos_out >= tau (compared in float)
  *   compute_idx [B,N] int32   ascending positions with reuse 0, -1 padded
  *   compute_len [B]   int32   their count
- * Requires W*sizeof(dtype) to be a multiple of 16 bytes, N <= 65536.
+ *   reuse_idx   [B,N] int32   (may be NULL) ascending positions with reuse 1,
+ *                             -1 padded: the cached list of the ragged
+ *                             attention over the recomputed tokens
+ *   reuse_len   [B]   int32   (NULL iff reuse_idx is) their count, N - compute_len
+ * Requires W*sizeof(dtype) to be a multiple of 16 bytes, N <= 65536.  Exactly
+ * one of reuse_idx, reuse_len NULL: MAR_E_NULL.
  */
 int mar_cos_gate(const void* x_cur, const void* x_cached, float tau, float eps,
                  float* cos_out, uint8_t* reuse_mask,
                  int32_t* compute_idx, int32_t* compute_len,
+                 int32_t* reuse_idx, int32_t* reuse_len,
                  int B, int N, int W, int dtype, void* stream);
 
 /*

@@ -196,12 +196,14 @@ def test_refresh_topk_noalloc_rejections(lib):
 
 def test_gate_and_cfg_rejections(lib):
     g = lib.mar_cos_gate
-    assert g(None, P, 0.95, 1e-8, P, P, P, P, 2, 10, 64, 1, None) == E_NULL
-    assert g(P, P, 0.95, 1e-8, P, P, P, P, 2, 10, 64, 5, None) == E_DTYPE
-    assert g(P, P, 0.95, 1e-8, P, P, P, P, 2, 0, 64, 1, None) == E_SHAPE
-    assert g(P, P, 0.95, 1e-8, P, P, P, P, 2, 10, 12, 1, None) == E_UNSUP      # 24-byte rows
-    assert g(P, P, float("nan"), 1e-8, P, P, P, P, 2, 10, 64, 1, None) == E_RANGE
-    assert g(P, P, 0.95, -1.0, P, P, P, P, 2, 10, 64, 1, None) == E_RANGE
+    assert g(None, P, 0.95, 1e-8, P, P, P, P, None, None, 2, 10, 64, 1, None) == E_NULL
+    assert g(P, P, 0.95, 1e-8, P, P, P, P, P, None, 2, 10, 64, 1, None) == E_NULL  # one of the pair
+    assert g(P, P, 0.95, 1e-8, P, P, P, P, None, P, 2, 10, 64, 1, None) == E_NULL
+    assert g(P, P, 0.95, 1e-8, P, P, P, P, None, None, 2, 10, 64, 5, None) == E_DTYPE
+    assert g(P, P, 0.95, 1e-8, P, P, P, P, P, P, 2, 0, 64, 1, None) == E_SHAPE
+    assert g(P, P, 0.95, 1e-8, P, P, P, P, None, None, 2, 10, 12, 1, None) == E_UNSUP  # 24-byte rows
+    assert g(P, P, float("nan"), 1e-8, P, P, P, P, None, None, 2, 10, 64, 1, None) == E_RANGE
+    assert g(P, P, 0.95, -1.0, P, P, P, P, None, None, 2, 10, 64, 1, None) == E_RANGE
     c = lib.mar_cfg_residual
     assert c(P, P, P, None, None, 1.0, 5, 16, None) == E_RANGE                   # bad mode
     assert c(P, None, P, None, None, 1.0, 0, 16, None) == E_NULL                 # store needs uncond

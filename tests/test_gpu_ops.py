@@ -200,16 +200,40 @@ def test_topk_full_size_mar_l(marca):
 # (under 1e-5 up to W = 4096).  A dropped 16-byte piece moves it by ~1e-3.
 GATE_COS_TOL = 1e-5
 
+
+def reuse_lists(mask):
+    """The ascending positions with reuse 1 of each row, -1 padded, and their
+    counts: the definition of the gate's optional reuse list, from a mask."""
+    B, N = mask.shape
+    idx = np.full((B, N), -1, np.int32)
+    cnt = np.zeros(B, np.int32)
+    for b in range(B):
+        pos = np.flatnonzero(mask[b])
+        idx[b, :len(pos)] = pos
+        cnt[b] = len(pos)
+    return idx, cnt
+
+
+def gate_with_reuse(marca, x, y, tau=0.95):
+    B, N = x.shape[0], x.shape[1]
+    ridx = torch.full((B, N), 7, dtype=torch.int32, device=DEV)  # stale values must be overwritten
+    rlen = torch.full((B,), 7, dtype=torch.int32, device=DEV)
+    cos, reuse, cidx, clen = marca.mar_cos_gate(x, y, tau, reuse_idx=ridx, reuse_len=rlen)
+    return cos, reuse, cidx, clen, ridx, rlen
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_gate_small_bit_exact(marca, dtype):
     x, y, rho = gate_features(3, 100, 256, seed=21, device=DEV, dtype=dtype)
-    cos, reuse, cidx, clen = marca.mar_cos_gate(x, y, 0.95)
+    cos, reuse, cidx, clen, ridx, rlen = gate_with_reuse(marca, x, y)
     torch.cuda.synchronize()
     c_gpu = cos.double().cpu().numpy()
     tau32 = float(np.float32(0.95))
     r2, c2, l2 = oracle.gate_from_cos(c_gpu, tau32)
     assert (reuse.cpu().numpy() == r2).all() and (cidx.cpu().numpy() == c2).all()
     assert (clen.cpu().numpy() == l2).all()
+    ri, rl = reuse_lists(r2)
+    assert (ridx.cpu().numpy() == ri).all() and (rlen.cpu().numpy() == rl).all()
+    assert (rl + l2 == 100).all()
     c_ref, r_ref, _, _ = oracle.cos_gate(x.double().cpu().numpy(), y.double().cpu().numpy(), tau32)
     assert np.abs(c_gpu - c_ref).max() <= GATE_COS_TOL
     away = np.abs(c_ref - tau32) > 1e-4
@@ -267,19 +291,24 @@ def test_gate_zero_and_parallel_vectors(marca):
     np.testing.assert_allclose(cos.cpu().numpy()[0], [0, 1, 0, -1], atol=1e-6)
     assert reuse.cpu().numpy()[0].tolist() == [0, 1, 0, 0]
     assert cidx.cpu().numpy()[0].tolist() == [0, 2, 3, -1] and int(clen[0]) == 3
+    _, _, _, _, ridx, rlen = gate_with_reuse(marca, x, y)
+    torch.cuda.synchronize()
+    assert ridx.cpu().numpy()[0].tolist() == [1, -1, -1, -1] and int(rlen[0]) == 1
 
 
 def test_gate_full_size_highres(marca):
     """512x512-equivalent: 64 sequences x 1088 tokens x W 1024, bf16; sampled oracle rows."""
     B, N, W = 64, 1088, 1024
     x, y, rho = device_gate_features(B, N, W, seed=1005, device=DEV)
-    cos, reuse, cidx, clen = marca.mar_cos_gate(x, y, 0.95)
+    cos, reuse, cidx, clen, ridx, rlen = gate_with_reuse(marca, x, y)
     torch.cuda.synchronize()
     c_gpu = cos.double().cpu().numpy()
     tau32 = float(np.float32(0.95))
     r2, c2, l2 = oracle.gate_from_cos(c_gpu, tau32)
     assert (reuse.cpu().numpy() == r2).all() and (cidx.cpu().numpy() == c2).all()
     assert (clen.cpu().numpy() == l2).all()
+    ri, rl = reuse_lists(r2)
+    assert (ridx.cpu().numpy() == ri).all() and (rlen.cpu().numpy() == rl).all()
     rows = [0, 17, 63]
     c_ref, r_ref, _, _ = oracle.cos_gate(x[rows].double().cpu().numpy(),
                                          y[rows].double().cpu().numpy(), tau32)
