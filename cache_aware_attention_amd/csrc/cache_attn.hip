@@ -1483,8 +1483,11 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
 //    through that XCD's L2.
 //  * UPDATE: the loading lanes write each chunk they load into the caches;
 //    of a unit's blocks, block c mod nb writes chunk c.
-//  * The per-chunk math is wg_chunk's.  Every load streams: a chunk is read
-//    again only by the other blocks of its unit, which run at the same time.
+//  * The per-chunk math is wg_chunk's.  Q rows load with streaming loads;
+//    so do K/V rows when a unit has one block (SHARED = false).  With several
+//    blocks (SHARED) the K/V loads are plain, since the unit's other blocks
+//    read the same chunks from L2 at about the same time (streaming loads
+//    there cost 3-4% at 1088 tokens; plain ones cost 4-5% at 320).
 // ---------------------------------------------------------------------------
 constexpr int kDenseQ = kWgWaves * 16 * kWgNqt;  // queries per item
 constexpr int kDenseLds = 4 * kWgTile + kDenseQ * kD * 2 + kWgWaves * 2048;
@@ -1492,7 +1495,7 @@ constexpr int kDensePerCu = 2;  // resident workgroups per compute unit (registe
 static_assert(kDenseLds <= 64 * 1024, "static LDS");
 static_assert(kDenseQ % kChunk == 0, "Q row blocks follow the chunks");
 
-template <bool UPDATE>
+template <bool UPDATE, bool SHARED>
 __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attn_dense_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict__ k_a,
                        const uint16_t* __restrict__ v_a, uint16_t* __restrict__ k_cache,
@@ -1524,8 +1527,13 @@ void attn_dense_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restr
     auto rsrc = [&](const uint16_t* base, int u) {
         return uniform_rsrc(base + static_cast<size_t>(u) * A * kD, unit_bytes);
     };
-    auto ld = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t ofs) __attribute__((always_inline)) {
+    // Q rows are read once: streaming loads.  K/V rows too, unless the unit
+    // has several blocks (SHARED), whose workgroups read them from L2 again.
+    auto ldq = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t ofs) __attribute__((always_inline)) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, ofs, 0, kStreamPolicy));
+    };
+    auto ld = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t ofs) __attribute__((always_inline)) {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, ofs, 0, SHARED ? 0 : kStreamPolicy));
     };
     // Loading lane: piece tid % 8 of row tid / 8 of a 32-row block.
     const int lrow = tid >> 3;
@@ -1550,7 +1558,7 @@ void attn_dense_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < kDenseQ / kChunk; ++i) {
             const int r = qb * kDenseQ + i * kChunk + lrow;  // a row past A reads zero
-            qv[i] = ld(rq, static_cast<uint32_t>(r) * (kD * 2) + piece);
+            qv[i] = ldq(rq, static_cast<uint32_t>(r) * (kD * 2) + piece);
         }
         const uint4 kk = ld(rsrc(k_a, u), static_cast<uint32_t>(lrow) * (kD * 2) + piece);
         const uint4 vv = ld(rsrc(v_a, u), static_cast<uint32_t>(lrow) * (kD * 2) + piece);
@@ -1612,7 +1620,7 @@ void attn_dense_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restr
             sk = ld(own ? rk : rkn, ofs);
             sv = ld(own ? rv : rvn, ofs);
             const bool qrow = sn >= 0 && c * kChunk < kDenseQ;  // uniform
-            sq = ld(rqn, qrow ? static_cast<uint32_t>(qbn * kDenseQ + c * kChunk) * (kD * 2) + row_ofs : kOut);
+            sq = ldq(rqn, qrow ? static_cast<uint32_t>(qbn * kDenseQ + c * kChunk) * (kD * 2) + row_ofs : kOut);
             if (nq > 0)
                 wg_chunk<NQT, false, decltype(full_tag)::value, decltype(first_tag)::value>(
                     st, lds + BI * 2 * kWgTile, lds + BI * 2 * kWgTile + kWgTile, kofs, vofs, c, A,
@@ -1707,8 +1715,12 @@ int launch_dense_wg(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_
     int cus = 0;
     if (const int st = compute_units(stream, &cus); st != MAR_OK) return st;
     const int grid = std::min(items, std::max(8, (kDensePerCu * cus) / 8 * 8));
-    hipLaunchKernelGGL((attn_dense_kernel<UPDATE>), dim3(grid), dim3(64 * kWgWaves), 0, stream,
-                       q_a, k_a, v_a, k_cache, v_cache, out, lse, units, A, nb, scale_log2);
+    if (nb == 1)
+        hipLaunchKernelGGL((attn_dense_kernel<UPDATE, false>), dim3(grid), dim3(64 * kWgWaves), 0,
+                           stream, q_a, k_a, v_a, k_cache, v_cache, out, lse, units, A, nb, scale_log2);
+    else
+        hipLaunchKernelGGL((attn_dense_kernel<UPDATE, true>), dim3(grid), dim3(64 * kWgWaves), 0,
+                           stream, q_a, k_a, v_a, k_cache, v_cache, out, lse, units, A, nb, scale_log2);
     return status_from_launch();
 }
 

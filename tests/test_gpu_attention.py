@@ -49,6 +49,19 @@ def oracle_units(x, units, Nc):
     return np.stack(outs), np.stack(lses)
 
 
+def torch_f32_all_units(x, Nc):
+    """Every unit's attention over [active rows ; cached rows] in float32 torch
+    operations on the device: the oracle's definition, for all units at once
+    (an any-size check beside the oracle's sampled units)."""
+    q = x["q_a"].float()
+    B, H, A, D = q.shape
+    gi = x["cached"][:, :Nc].long()[:, None, :, None].expand(B, H, Nc, D)
+    k = torch.cat([x["k_a"].float(), torch.gather(x["k_cache"].float(), 2, gi)], 2)
+    v = torch.cat([x["v_a"].float(), torch.gather(x["v_cache"].float(), 2, gi)], 2)
+    s = torch.matmul(q, k.transpose(-1, -2).contiguous()) * D ** -0.5
+    return torch.matmul(torch.softmax(s, -1), v)
+
+
 def check(got_out, got_lse, ref_out, ref_lse, dtype):
     if dtype == "f32":
         for u in range(ref_out.shape[0]):
@@ -276,7 +289,8 @@ def test_full_attention_several_items_per_workgroup(marca, B, H, N, update):
 @pytest.mark.parametrize("name", ["mar_b", "mar_l", "mar_h", "highres"])
 def test_full_size_sampled_units(marca, name):
     """Full-size MAR shapes, the launch configuration the benchmark times;
-    the oracle checks the first and last (b,h) units and six seeded ones."""
+    the oracle checks the first and last (b,h) units and six seeded ones, and
+    a float32 torch computation of the same definition checks every unit."""
     cfg = CONFIGS[name]
     x = attention_inputs(cfg, DEV)
     out, lse = run(marca, x)
@@ -291,6 +305,10 @@ def test_full_size_sampled_units(marca, name):
     vmax = max(float(x["v_a"].float().abs().max()), float(x["v_cache"].float().abs().max()))
     assert float(out.float().abs().max()) <= vmax * (1 + 2 ** -6)
     assert torch.isfinite(out.float()).all()
+    # every unit against the same definition in float32 torch operations
+    ref_all = torch_f32_all_units(x, cfg.Nc)
+    assert float((out.float() - ref_all).abs().max()) <= 2e-2
+    del ref_all
 
 
 def test_deterministic(marca):
