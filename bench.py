@@ -430,9 +430,12 @@ def other_configs(marca, dev, stream):
 
 
 C5_ROUNDS = 3
+# the gated layers' attention and cache update in one call (the default), or
+# as the ragged attention followed by the scatter (--c5-separate-update)
+C5_FUSED_UPDATE = [True]
 
 
-def c5_decode(marca, dev, stream, rounds=C5_ROUNDS):
+def c5_decode(marca, dev, stream, rounds=C5_ROUNDS, modes=("cache", "none", "cache+cond")):
     """The high-res configuration's whole 64-step decode of the attention path
     at full size: 64 sequences (32 images x 2 CFG), 16 heads, 1088 tokens (64
     prefix + 1024 image), 32 layers, active budget 128, a refresh every third
@@ -443,10 +446,11 @@ def c5_decode(marca, dev, stream, rounds=C5_ROUNDS):
     kernel);
     layer 3 the fused cache-aware attention + cache update of its 128 active
     rows; layers 4-32 the gate (which also lists each sequence's reused
-    positions), the ragged attention of each sequence's recomputed tokens
-    over their fresh K/V and the cached K/V of its reused tokens, and the
-    scatter of the recomputed rows into the layer's cache; the CFG residual
-    reuse.  A refresh step runs full attention in every layer, layers 3-32
+    positions), and the ragged attention of each sequence's recomputed
+    tokens over their fresh K/V and the cached K/V of its reused tokens,
+    fused with the cache update of the recomputed rows
+    (mar_cache_attn_fwd_ragged_update; --c5-separate-update runs the ragged
+    attention and then the scatter instead); the CFG residual reuse.  A refresh step runs full attention in every layer, layers 3-32
     rewriting their caches in the same call, and stores the CFG residual.
     Modes as for MAR-L: no caches (full attention everywhere), the caches,
     and the caches + condition cache (the steps between refreshes compute the
@@ -557,11 +561,16 @@ def c5_decode(marca, dev, stream, rounds=C5_ROUNDS):
                 reuse_mask=gate_out["reuse"], compute_idx=gate_out["cidx"],
                 compute_len=gate_out["clen"], reuse_idx=gate_out["ridx"],
                 reuse_len=gate_out["rlen"], stream=stream)
-            run(("ragged", i), marca.mar_cache_attn_fwd_ragged, qc[i], kcn[i], vcn[i], kc[i],
-                vc[i], gate_out["ridx"], gate_out["clen"], gate_out["rlen"], out=outc[i],
-                stream=stream)
-            run(("scatter", i), marca.mar_kv_scatter_refresh, kc[i], vc[i], kcn[i], vcn[i],
-                gate_out["cidx"], stream=stream)
+            if C5_FUSED_UPDATE[0]:
+                run(("ragged_update", i), marca.mar_cache_attn_fwd_ragged_update, qc[i], kcn[i],
+                    vcn[i], kc[i], vc[i], gate_out["ridx"], gate_out["cidx"], gate_out["clen"],
+                    gate_out["rlen"], out=outc[i], stream=stream)
+            else:
+                run(("ragged", i), marca.mar_cache_attn_fwd_ragged, qc[i], kcn[i], vcn[i], kc[i],
+                    vc[i], gate_out["ridx"], gate_out["clen"], gate_out["rlen"], out=outc[i],
+                    stream=stream)
+                run(("scatter", i), marca.mar_kv_scatter_refresh, kc[i], vc[i], kcn[i], vcn[i],
+                    gate_out["cidx"], stream=stream)
         run(("cfg_reuse",), marca.mar_cfg_residual, cond, residual=residual,
             mode=marca.MAR_CFG_REUSE, uncond_out=uncond_out, stream=stream)
 
@@ -584,7 +593,6 @@ def c5_decode(marca, dev, stream, rounds=C5_ROUNDS):
             cached_step(t)
             half[0] = B
 
-    modes = ("cache", "none", "cache+cond")
     samples = {m: [] for m in modes}
     for m in modes:
         decode(m)
@@ -600,17 +608,20 @@ def c5_decode(marca, dev, stream, rounds=C5_ROUNDS):
             torch.cuda.synchronize()
             samples[m].append(e0.elapsed_time(e1))
     med = {m: sorted(v)[len(v) // 2] for m, v in samples.items()}
+    ms = lambda m: med.get(m)
+    ratio = lambda a, b: (med[a] / med[b]) if a in med and b in med else None
     res = {
         "what": " ".join(c5_decode.__doc__.split()),
         "sequences": B, "heads": H, "tokens": N, "layers": L, "budget": cfg.budget,
         "gate_width": cfg.W, "gated_layers": n_gated, "steps": cfg.steps,
         "refresh_steps": sum(p.refresh for p in plans),
         "recomputed_rows_capacity": acap[1:],
+        "gated_layer_update": "fused" if C5_FUSED_UPDATE[0] else "separate scatter",
         "timing": f"median of {rounds} interleaved runs per mode",
         "samples_ms": samples,
-        "ms": med["cache"], "ms_no_cache": med["none"], "ms_cond_cache": med["cache+cond"],
-        "speedup": med["none"] / med["cache"],
-        "speedup_cond_cache": med["none"] / med["cache+cond"],
+        "ms": ms("cache"), "ms_no_cache": ms("none"), "ms_cond_cache": ms("cache+cond"),
+        "speedup": ratio("none", "cache"),
+        "speedup_cond_cache": ratio("none", "cache+cond"),
         "setup_s": setup_s,
     }
     del kc, vc, gx, gy, qc, kcn, vcn, prep
@@ -628,6 +639,10 @@ def main():
                     help="skip the whole-decode timing (for counter runs)")
     ap.add_argument("--c5-only", action="store_true",
                     help="only the full-size high-res 64-step decode (one JSON object)")
+    ap.add_argument("--c5-modes", default="cache,none,cache+cond",
+                    help="with --c5-only: the decode modes to run (comma-separated)")
+    ap.add_argument("--c5-separate-update", action="store_true",
+                    help="with --c5-only: the gated layers' cache update as a separate scatter")
     ap.add_argument("--locality-only", action="store_true",
                     help="only the locality comparison's kernels, a fixed sequence (counter runs)")
     ap.add_argument("--copy-only", action="store_true",
@@ -649,7 +664,12 @@ def main():
     cfg = CONFIGS["mar_l"]
 
     if args.c5_only:
-        print(json.dumps(c5_decode(marca, dev, torch.cuda.current_stream())))
+        C5_FUSED_UPDATE[0] = not args.c5_separate_update
+        modes = tuple(m for m in args.c5_modes.split(",") if m)
+        if not modes or any(m not in ("cache", "none", "cache+cond") for m in modes):
+            print(f"bench: unknown --c5-modes {args.c5_modes!r}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(c5_decode(marca, dev, torch.cuda.current_stream(), modes=modes)))
         return
 
     if args.locality_only:

@@ -67,6 +67,9 @@ def load_library(path: Optional[str] = None):
     lib.mar_cache_attn_fwd_update.restype = I
     lib.mar_cache_attn_fwd_update.argtypes = [V, V, V, V, V, V, I, V, I, V, V, V, I, I, I, I, I,
                                               I, F, I, V]
+    lib.mar_cache_attn_fwd_ragged_update.restype = I
+    lib.mar_cache_attn_fwd_ragged_update.argtypes = [V, V, V, V, V, V, I, V, I, V, V, V, V, V, I,
+                                                     I, I, I, I, I, F, I, V]
     lib.mar_cache_attn_fwd_scores.restype = I
     lib.mar_cache_attn_fwd_scores.argtypes = [V, V, V, V, V, V, I, I, V, S, I, I, I, I, F, I, V]
     lib.mar_refresh_select.restype = I
@@ -243,6 +246,48 @@ def mar_cache_attn_fwd_ragged(q_a, k_a, v_a, k_cache, v_cache, cached_idx, a_len
         _dev(v_cache, "v_cache"), cptr, ldc, _dev(a_len, "a_len"), _dev(c_len, "c_len"),
         _dev(out, "out"), _dev(lse, "lse") if lse is not None else None, B, H, N, A, ldc, D,
         float(scale), code, _stream(stream))
+    return out
+
+
+def mar_cache_attn_fwd_ragged_update(q_a, k_a, v_a, k_cache, v_cache, cached_idx, active_idx,
+                                     a_len, c_len, out=None, lse=None, err_count=None, scale=None,
+                                     stream=None):
+    """mar_cache_attn_fwd_ragged, plus each sequence's first a_len[b] rows of
+    k_a/v_a written into k_cache/v_cache at active_idx [B, ld] (entries at or
+    past a_len[b] are not read) in the same pass.  Returns out."""
+    B, H, A, D = q_a.shape
+    N = k_cache.shape[2]
+    dt = q_a.dtype
+    code = _dtype_code(q_a)
+    for name, t in (("k_a", k_a), ("v_a", v_a)):
+        _dev(t, name, dt, (B, H, A, D))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, name, dt, (B, H, N, D))
+    if cached_idx is None:
+        ldc, cptr = 0, None
+    else:
+        if cached_idx.dim() != 2 or cached_idx.shape[0] != B:
+            raise ValueError("cached_idx must be [B, ldc]")
+        ldc = cached_idx.shape[1]
+        cptr = _dev(cached_idx, "cached_idx", torch.int32)
+    if active_idx.dim() != 2 or active_idx.shape[0] != B:
+        raise ValueError("active_idx must be [B, ld_act]")
+    for name, t in (("a_len", a_len), ("c_len", c_len)):
+        _dev(t, name, torch.int32, (B,))
+    if out is None:
+        out = torch.zeros_like(q_a)
+    _dev(out, "out", dt, (B, H, A, D))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, H, A))
+    if scale is None:
+        scale = D ** -0.5
+    _call("mar_cache_attn_fwd_ragged_update",
+        _dev(q_a, "q_a"), _dev(k_a, "k_a"), _dev(v_a, "v_a"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), cptr, ldc, _dev(active_idx, "active_idx", torch.int32),
+        active_idx.shape[1], _dev(a_len, "a_len"), _dev(c_len, "c_len"),
+        _dev(err_count, "err_count", torch.int32), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else None, B, H, N, A, ldc, D, float(scale), code,
+        _stream(stream))
     return out
 
 

@@ -12,6 +12,7 @@ constexpr int kHeadDim = 64;
 constexpr int kMaxTopkTokens = 4096;
 constexpr int kMaxGenQueries = 64;
 constexpr int kMaxGateTokens = 65536;
+constexpr int kMaxRaggedUpdateTokens = 8192;  // the MFMA attention kernels' limit
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int elem_bytes(int dtype) { return dtype == MAR_F32 ? 4 : (dtype == MAR_BF16 ? 2 : 0); }
@@ -79,6 +80,26 @@ extern "C" int mar_cache_attn_fwd_ragged(const void* q_a, const void* k_a, const
     return marca::launch_cache_attn_ragged(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc,
                                            a_len, c_len, out, lse, B, H, N, A, Nc, scale, dtype,
                                            stream);
+}
+
+extern "C" int mar_cache_attn_fwd_ragged_update(const void* q_a, const void* k_a,
+                                                const void* v_a, void* k_cache, void* v_cache,
+                                                const int32_t* cached_idx, int ldc,
+                                                const int32_t* active_idx, int ld_act,
+                                                const int32_t* a_len, const int32_t* c_len,
+                                                int32_t* err_count, void* out, float* lse, int B,
+                                                int H, int N, int A, int Nc, int D, float scale,
+                                                int dtype, void* stream) {
+    if (!active_idx || !a_len || !c_len) return MAR_E_NULL;
+    const int st = check_cache_attn(q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, B, H,
+                                    N, A, Nc, D, scale, dtype, true);
+    if (st != MAR_OK) return st;
+    if (ld_act < A) return MAR_E_SHAPE;
+    if (dtype != MAR_BF16 || A < 16 || N > kMaxRaggedUpdateTokens) return MAR_E_UNSUPPORTED;
+    return marca::launch_cache_attn_ragged_update(q_a, k_a, v_a, k_cache, v_cache, cached_idx,
+                                                  ldc, active_idx, ld_act, a_len, c_len,
+                                                  err_count, out, lse, B, H, N, A, Nc, scale,
+                                                  stream);
 }
 
 extern "C" int mar_cache_attn_fwd_update(const void* q_a, const void* k_a, const void* v_a,

@@ -862,7 +862,8 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
 //    first block write the active rows into the caches at active_idx.
 //    RAGGED: per-sequence counts, min(a_len[b], A) active rows and
 //    min(c_len[b], Nc) cached entries (A and Nc stay the row stride and the
-//    list capacity); rows past a sequence's active count are not written.
+//    list capacity); rows past a sequence's active count are not written,
+//    neither to out nor (with UPDATE) to the caches.
 // The MFMA tiles are those of attn_mfma_kernel.  The softmax state differs:
 //  * each query keeps one reference mc, a maximum of its scaled scores
 //    s * scale_log2, set from the first chunk (active rows, at least the
@@ -1084,7 +1085,7 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
                     const int32_t* __restrict__ gen_idx = nullptr, int ld_gen = 0, int G = 0,
                     float* __restrict__ partials = nullptr) {
     static_assert(W == 1 || W == 2 || W == 4, "waves per workgroup");
-    static_assert(!RAGGED || (CACHED && !UPDATE), "per-sequence counts: cached rows, no update");
+    static_assert(!RAGGED || CACHED, "per-sequence counts: cached rows");
     static_assert(!SCORES || (!CACHED && !UPDATE && W == 4), "scores: layer 2's full attention");
     static_assert(CACHED || SCORES, "the full-attention layers run attn_dense_kernel");
     constexpr int kQ = 16 * NQT;         // queries per wave
@@ -1190,7 +1191,7 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
             constexpr int kNT = 2;  // nontemporal (streaming) store
             const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(k_cache + cb, N * kD * 2);
             const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(v_cache + cb, N * kD * 2);
-            if (c * kChunk < A) {  // uniform
+            if (c * kChunk < An) {  // uniform: the chunk holds active rows
 #pragma unroll
                 for (int p = 0; p < kPasses; ++p) {
                     const int r = c * kChunk + 8 * W * p + lrow;
@@ -1267,8 +1268,13 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
         if constexpr (UPDATE) {
             // Only the unit's first block writes the active rows; an entry
             // outside [0, N) is skipped and, once per sequence, counted.
+            // RAGGED: entries past the sequence's count are not read.
             const int32_t* ag = active_idx + static_cast<size_t>(b) * ld_act;
             for (int r = tid; r < A; r += 64 * W) {
+                if (r >= An) {
+                    aidx_s[r] = -1;
+                    continue;
+                }
                 const int n = ag[r];
                 const bool ok = n >= 0 && n < N;
                 aidx_s[r] = (ok && qb == 0) ? n : -1;
@@ -1759,20 +1765,27 @@ int launch_cached_wg(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v
                      const int32_t* a_len, const int32_t* c_len, hipStream_t stream) {
     const int units = B * H;
     const size_t lds = cached_wg_lds(UPDATE, A, Nc);  // <= kCachedWgMaxLds (checked by the caller)
-    auto go = [&](auto waves_tag) {
+    auto go = [&](auto nqt_tag, auto waves_tag) {
+        constexpr int kNqt = decltype(nqt_tag)::value;
         constexpr int kW = decltype(waves_tag)::value;
-        constexpr int kPerBlock = kW * 64;
+        constexpr int kPerBlock = kW * 16 * kNqt;
         const int nb = (A + kPerBlock - 1) / kPerBlock;
         const int grid = (nb == 1) ? units : ((units + 7) / 8) * 8 * nb;
-        hipLaunchKernelGGL((attn_wg_kernel<4, kW, UPDATE, true, RAGGED>), dim3(grid), dim3(64 * kW),
-                           lds, stream, q_a, k_a, v_a, const_cast<uint16_t*>(k_cache),
-                           const_cast<uint16_t*>(v_cache), out, lse, units, A, nb, scale_log2,
-                           cached_idx, ldc, H, N, Nc, active_idx, ld_act, err_count, a_len,
-                           c_len);
+        hipLaunchKernelGGL((attn_wg_kernel<kNqt, kW, UPDATE, true, RAGGED>), dim3(grid),
+                           dim3(64 * kW), lds, stream, q_a, k_a, v_a,
+                           const_cast<uint16_t*>(k_cache), const_cast<uint16_t*>(v_cache), out,
+                           lse, units, A, nb, scale_log2, cached_idx, ldc, H, N, Nc, active_idx,
+                           ld_act, err_count, a_len, c_len);
         return status_from_launch();
     };
-    // two waves up to 128 queries, four beyond (more blocks past 256)
-    return (A <= 2 * 64) ? go(std::integral_constant<int, 2>{}) : go(std::integral_constant<int, 4>{});
+    using Q4 = std::integral_constant<int, 4>;
+    // two waves up to 128 queries, four beyond (more blocks past 256).  (With
+    // per-sequence counts, four waves of 48 queries instead, so that a block
+    // whose counts sit below the capacity leaves fewer tile slots empty, made
+    // the high-res gated layers slower: their sequences past 192 queries then
+    // stream the unit's K/V a second time.)
+    return (A <= 2 * 64) ? go(Q4{}, std::integral_constant<int, 2>{})
+                         : go(Q4{}, std::integral_constant<int, 4>{});
 }
 template <int NQT, bool UPDATE>
 int launch_mfma(const uint16_t* q_a, const uint16_t* k_a, const uint16_t* v_a,
@@ -1928,10 +1941,9 @@ int dispatch_mfma(const uint16_t* q, const uint16_t* ka, const uint16_t* va, con
             return launch_cached_wg<UPDATE, false>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B,
                                                    H, N, A, Nc, scale_log2, active_idx, ld_act,
                                                    err_count, nullptr, nullptr, stream);
-        if constexpr (!UPDATE)
-            return launch_cached_wg<false, true>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H,
-                                                 N, A, Nc, scale_log2, active_idx, ld_act,
-                                                 err_count, a_len, c_len, stream);
+        return launch_cached_wg<UPDATE, true>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N,
+                                              A, Nc, scale_log2, active_idx, ld_act, err_count,
+                                              a_len, c_len, stream);
     }
     const int nqt = (n_groups > 1) ? 4 : (A + 15) / 16;
     switch (nqt) {
@@ -2043,6 +2055,22 @@ int launch_cache_attn_update(const void* q_a, const void* k_a, const void* v_a, 
     const int row_bytes = kD * (dtype == MAR_BF16 ? 2 : 4);
     return launch_kv_scatter(k_cache, v_cache, k_a, v_a, active_idx, ld_act, err_count, B, H, N,
                              A, row_bytes, stream_v);
+}
+
+int launch_cache_attn_ragged_update(const void* q_a, const void* k_a, const void* v_a,
+                                    void* k_cache, void* v_cache, const int32_t* cached_idx,
+                                    int ldc, const int32_t* active_idx, int ld_act,
+                                    const int32_t* a_len, const int32_t* c_len,
+                                    int32_t* err_count, void* out, float* lse, int B, int H,
+                                    int N, int A, int Nc, float scale, void* stream_v) {
+    // bf16, A >= 16, N <= kMaxMfmaTokens (checked by the caller): the MFMA
+    // kernels, whose per-sequence instantiations write rows [0, An) only.
+    return dispatch_mfma<true>(
+        static_cast<const uint16_t*>(q_a), static_cast<const uint16_t*>(k_a),
+        static_cast<const uint16_t*>(v_a), static_cast<const uint16_t*>(k_cache),
+        static_cast<const uint16_t*>(v_cache), cached_idx, ldc, static_cast<uint16_t*>(out), lse,
+        B, H, N, A, Nc, scale * kLog2e, active_idx, ld_act, err_count, a_len, c_len,
+        static_cast<hipStream_t>(stream_v));
 }
 
 }  // namespace marca

@@ -27,6 +27,12 @@ int launch_cache_attn_update(const void* q_a, const void* k_a, const void* v_a, 
                              const int32_t* active_idx, int ld_act, int32_t* err_count, void* out,
                              float* lse, int B, int H, int N, int A, int Nc, float scale,
                              int dtype, void* stream);
+int launch_cache_attn_ragged_update(const void* q_a, const void* k_a, const void* v_a,
+                                    void* k_cache, void* v_cache, const int32_t* cached_idx,
+                                    int ldc, const int32_t* active_idx, int ld_act,
+                                    const int32_t* a_len, const int32_t* c_len,
+                                    int32_t* err_count, void* out, float* lse, int B, int H,
+                                    int N, int A, int Nc, float scale, void* stream);
 
 // Layer 2's full attention (A = N <= 320, no cached rows, bf16) that also
 // writes the generating queries' per-head probability sums into partials.

@@ -154,6 +154,36 @@ int mar_cache_attn_fwd_update(const void* q_a, const void* k_a, const void* v_a,
                               float scale, int dtype, void* stream);
 
 /*
+ * The per-sequence form of mar_cache_attn_fwd_update, for LazyMAR's token
+ * cache ([LazyMAR] Key designs, token cache: each sequence recomputes the
+ * tokens its gate selects, and their fresh K/V replace the cached ones;
+ * [MARche] Key Design 2, Eq. 1-2, for the attention).
+ *
+ * Computes exactly what mar_cache_attn_fwd_ragged computes (a_len, c_len and
+ * the capacities A, Nc as there) and, in the same pass, writes each
+ * sequence's fresh active rows into the caches:
+ *   k_cache[b,h,active_idx[b*ld_act+i],:] = k_a[b,h,i,:]  (and V),  i < An
+ * where An = min(max(a_len[b], 0), A).  Entries of active_idx at or past a
+ * sequence's An are not read (the gate's compute list, -1 padded, passes as
+ * is); an entry before An outside [0,N) is skipped and, with err_count
+ * non-NULL, counted once per sequence.
+ * Precondition as for mar_cache_attn_fwd_update: a sequence's first An
+ * active positions are distinct and none of them is among its first
+ * min(c_len[b], Nc) cached entries.  Requires bf16 (MAR_E_UNSUPPORTED
+ * otherwise), D == 64, 16 <= A (MAR_E_UNSUPPORTED), N <= 8192, ld_act >= A,
+ * plus the requirements of mar_cache_attn_fwd_ragged; active_idx, a_len and
+ * c_len must not be NULL (MAR_E_NULL).
+ */
+int mar_cache_attn_fwd_ragged_update(const void* q_a, const void* k_a, const void* v_a,
+                                     void* k_cache, void* v_cache,
+                                     const int32_t* cached_idx, int ldc,
+                                     const int32_t* active_idx, int ld_act,
+                                     const int32_t* a_len, const int32_t* c_len,
+                                     int32_t* err_count, void* out, float* lse,
+                                     int B, int H, int N, int A, int Nc, int D,
+                                     float scale, int dtype, void* stream);
+
+/*
  * Layer-2 full attention that also emits the refresh relevance partials
  * ([MARche] Key Design 1 and figure 3 on the Pith page: the refreshing tokens
  * are ranked by layer 2's attention from the generating tokens to every

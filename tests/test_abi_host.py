@@ -194,6 +194,19 @@ def test_refresh_topk_noalloc_rejections(lib):
     assert f(P, P, P, 4, 4, 4, 0.125, P, P, 8, P, 320, P, 1024, 16, 4, 320, 64, 1, None) == E_WS
 
 
+def test_ragged_update_rejections(lib):
+    f = lib.mar_cache_attn_fwd_ragged_update
+    # q k v kc vc cached ldc act ld_act a_len c_len err out lse B H N A Nc D scale dtype stream
+    ok = (P, P, P, P, P, P, 8, P, 32, P, P, None, P, None, 2, 2, 64, 32, 8, 64, 0.125, 1, None)
+    assert f(*ok[:7], None, *ok[8:]) == E_NULL                          # no active list
+    assert f(*ok[:9], None, *ok[10:]) == E_NULL                         # no a_len
+    assert f(*ok[:10], None, *ok[11:]) == E_NULL                        # no c_len
+    assert f(*ok[:8], 31, *ok[9:]) == E_SHAPE                           # ld_act < A
+    assert f(*ok[:21], 0, None) == E_UNSUP                              # fp32
+    assert f(*ok[:8], 8, *ok[9:17], 8, *ok[18:]) == E_UNSUP             # A < 16
+    assert f(*ok[:17], 65, *ok[18:]) == E_SHAPE                         # capacity above N
+
+
 def test_gate_and_cfg_rejections(lib):
     g = lib.mar_cos_gate
     assert g(None, P, 0.95, 1e-8, P, P, P, P, None, None, 2, 10, 64, 1, None) == E_NULL

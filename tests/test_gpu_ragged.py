@@ -39,7 +39,7 @@ def oracle_seq(q, ka, va, kc, vc, cached, b, h, an, cn, scale):
 
 
 @pytest.mark.parametrize("dtype,A,Nc", [("bf16", 64, 250), ("bf16", 100, 200), ("f32", 40, 120),
-                                        ("bf16", 12, 90)])
+                                        ("bf16", 12, 90), ("bf16", 200, 700), ("bf16", 256, 500)])
 def test_ragged_lengths(marca, dtype, A, Nc):
     B, H, N, D = 5, 2, A + Nc + 10, 64
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -120,3 +120,64 @@ def test_lazymar_token_cache_chain(marca):
         for h in range(H):
             o, _ = oracle_seq(q_a, k_a, v_a, kc, vc, cached, b, h, an, cn, D ** -0.5)
             assert np.abs(f64(out[b, h, :an]) - o).max() <= 2e-2, (b, h)
+
+
+def raw(t):
+    return t.detach().contiguous().cpu().view(torch.int16).numpy()
+
+
+@pytest.mark.parametrize("B,H,A,Nc", [(5, 2, 64, 250), (5, 2, 100, 200), (5, 2, 200, 700),
+                                      (1, 2, 40, 300)])
+def test_ragged_update(marca, B, H, A, Nc):
+    """mar_cache_attn_fwd_ragged_update: the output of mar_cache_attn_fwd_ragged
+    bit for bit, and each sequence's first a_len[b] fresh rows written into the
+    caches at active_idx (the oracle's scatter on the list cut at a_len[b]);
+    entries past a_len[b] are padding that is never read, and a bad entry
+    before it is skipped and counted once per sequence.  The shapes take the
+    one-wave kernel (64 queries), the cached workgroup kernel with two and with
+    four waves, and the split kernel (two units)."""
+    import oracle
+    D = 64
+    N = A + Nc + 10
+    q, ka, va = (device_normal((B, H, A, D), 40 + i, DEV, torch.bfloat16) for i in range(3))
+    kc, vc = (device_normal((B, H, N, D), 50 + i, DEV, torch.bfloat16) for i in range(2))
+    g = torch.Generator().manual_seed(A * 7 + Nc)
+    a_len = torch.tensor([A, 0, A // 2 + 1, 1, A - 3][:B], dtype=torch.int32)
+    c_len = torch.tensor([Nc, Nc // 3, 0, Nc, 5][:B], dtype=torch.int32)
+    act = torch.full((B, A + 3), -1, dtype=torch.int32)      # ld_act > A
+    cached = torch.full((B, Nc), -1, dtype=torch.int32)
+    bad = 0
+    for b in range(B):
+        perm = torch.randperm(N, generator=g).to(torch.int32)
+        an = int(a_len[b])
+        act[b, :A] = perm[:A]
+        cached[b] = perm[A:A + Nc]
+        act[b, an:A] = 77777  # padding past the sequence's count: never read
+        if b == 0 and an > 3:
+            act[b, 2] = N + 5  # a bad entry before the count: skipped, counted
+            bad += 1
+    act_d, cached_d = act.to(DEV), cached.to(DEV)
+    a_d, c_d = a_len.to(DEV), c_len.to(DEV)
+    ref = marca.mar_cache_attn_fwd_ragged(q, ka, va, kc, vc, cached_d, a_d, c_d)
+    k0, v0 = raw(kc), raw(vc)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = marca.mar_cache_attn_fwd_ragged_update(q, ka, va, kc, vc, cached_d, act_d, a_d, c_d,
+                                                 err_count=err)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    idx = act[:, :A].clone()
+    for b in range(B):
+        idx[b, int(a_len[b]):] = -1
+    kr, vr, skipped = oracle.kv_scatter(k0, v0, raw(ka), raw(va), idx.numpy())
+    assert np.array_equal(raw(kc), kr) and np.array_equal(raw(vc), vr)
+    assert int(err.item()) == bad
+    assert skipped == bad + int((A - a_len).sum())
+    # the attention itself against the oracle on one sampled head per sequence
+    for b in range(B):
+        an, cn = int(a_len[b]), int(c_len[b])
+        if an == 0:
+            continue
+        o, _ = oracle_seq(q, ka, va, torch.from_numpy(k0).view(torch.bfloat16).to(DEV),
+                          torch.from_numpy(v0).view(torch.bfloat16).to(DEV), cached_d, b, b % H,
+                          an, cn, D ** -0.5)
+        assert np.abs(f64(out[b, b % H, :an]) - o).max() <= 2e-2, b
