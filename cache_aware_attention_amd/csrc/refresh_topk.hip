@@ -454,17 +454,19 @@ __device__ __forceinline__ uint64_t rank_key(float s, int j) {
 // tokens in (score descending, index ascending) order.  Each wave ranks
 // tokens w, w + kSelWaves, ...; lane l holds keys l, l + 64, ... and one
 // ballot per 64 keys counts the larger ones.
-// NB > 0 (N <= 64 NB <= 512, at most one token per thread): all keys sit in NB
-// registers per lane, so the ballots need no bounds test; four tokens are
-// ranked per step, which keeps four independent compare / count chains in
-// flight, and the ascending compaction takes its positions from a ballot
-// per wave.  NB == 0 is the general form for longer sequences.
+// NB > 0 (N <= 64 NB <= 2048): all keys sit in NB registers per lane, so the
+// ballots need no bounds test; four tokens are ranked per step, which keeps
+// four independent compare / count chains in flight, and the ascending
+// compaction takes its positions from a ballot per wave.  A wave ranks at
+// most 64 tokens (one per lane) per round and a thread compacts one token
+// per round: one round up to 1024 tokens, two up to 2048.  NB == 0 is the
+// general form for longer sequences, which reads the keys past the first 512
+// from LDS inside the counting loop.
 constexpr int kSelThreads = 1024;  // 16 waves: more compare / count chains in flight per CU
 constexpr int kSelWaves = kSelThreads / kWave;
-// NB <= 8 register blocks cover up to 512 tokens: with at least 512 threads
-// each token has a thread in the compaction, and with at least 8 waves each
-// wave ranks at most 64 tokens (one per lane) in the ranking loop.
-static_assert(kSelThreads >= 8 * kWave, "selection: the register-block path needs 512 threads");
+constexpr int kSelMaxRegBlocks = 32;  // the register-block path: up to 2048 tokens
+static_assert(kSelThreads == kSelWaves * kWave && kSelWaves * kWave * 2 >= kSelMaxRegBlocks * kWave,
+              "selection: two rounds of one token per thread cover the register-block path");
 template <int NB>
 __global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ gp_idx, int ld_gp, int n_gp, int K,
@@ -511,61 +513,76 @@ __global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
 
     int32_t* crow = cached_idx + (size_t)b * ld_cached;
     if constexpr (NB > 0) {
+        static_assert(NB <= kSelMaxRegBlocks, "register blocks");
+        constexpr int kRounds = (NB * kWave + kSelThreads - 1) / kSelThreads;  // 1 or 2
         uint64_t kr[NB];
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             const int i = lane + kWave * k;
             kr[k] = (i < N) ? keys[i] : 0ull;  // 0 is never larger than an eligible key
         }
-        // Lane l holds the key of token wu + kSelWaves * l.  Tokens at or past
-        // N read key 0 and are skipped like ineligible ones; nt <= 64, so the
-        // lane index of every step stays below 64.
+        // Round rd: lane l holds the key of token base + kSelWaves * l, base =
+        // wu + kSelThreads * rd.  Tokens at or past N read key 0 and are
+        // skipped like ineligible ones; nt <= 64, so the lane index of every
+        // step stays below 64.
         const int wu = __builtin_amdgcn_readfirstlane(w);
-        const int jl = wu + kSelWaves * lane;
-        const uint64_t kl = (jl < N) ? keys[jl] : 0ull;
-        const int nt = (N - wu + kSelWaves - 1) / kSelWaves;
-        for (int e0 = 0; e0 < nt; e0 += 4) {
-            uint64_t kj[4];
-            int cnt[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(kl), e0 + q);
-                const uint32_t hi =
-                    __builtin_amdgcn_readlane(static_cast<uint32_t>(kl >> 32), e0 + q);
-                kj[q] = (static_cast<uint64_t>(hi) << 32) | lo;
-                cnt[q] = 0;
-            }
+        for (int rd = 0; rd < kRounds; ++rd) {
+            const int base = wu + kSelThreads * rd;
+            const int jl = base + kSelWaves * lane;
+            const uint64_t kl = (jl < N) ? keys[jl] : 0ull;
+            const int nt = (N > base) ? min(kWave, (N - base + kSelWaves - 1) / kSelWaves) : 0;
+            for (int e0 = 0; e0 < nt; e0 += 4) {
+                uint64_t kj[4];
+                int cnt[4];
 #pragma unroll
-            for (int k = 0; k < NB; ++k)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) cnt[q] += __popcll(__ballot(kr[k] > kj[q]));
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (kj[q] != 0 && cnt[q] < K && lane == 0) {
-                    const int j = wu + kSelWaves * (e0 + q);
-                    arow[n_gp + cnt[q]] = j;
-                    state[j] = 2;
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(kl), e0 + q);
+                    const uint32_t hi =
+                        __builtin_amdgcn_readlane(static_cast<uint32_t>(kl >> 32), e0 + q);
+                    kj[q] = (static_cast<uint64_t>(hi) << 32) | lo;
+                    cnt[q] = 0;
                 }
+#pragma unroll
+                for (int k = 0; k < NB; ++k)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) cnt[q] += __popcll(__ballot(kr[k] > kj[q]));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (kj[q] != 0 && cnt[q] < K && lane == 0) {
+                        const int j = base + kSelWaves * (e0 + q);
+                        arow[n_gp + cnt[q]] = j;
+                        state[j] = 2;
+                    }
+            }
         }
         __syncthreads();
 
-        // Ascending compaction: thread tid holds token tid.
-        const bool c = tid < N && state[tid] == 0;
-        const uint64_t m = __ballot(c);
-        const int below = __builtin_amdgcn_mbcnt_hi(
-            static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
-        if (lane == 0) scan_scratch[w] = __popcll(m);
-        __syncthreads();
-        int pos = below, total = 0;
+        // Ascending compaction: in round rd thread tid holds token
+        // tid + kSelThreads * rd; a round's positions follow the earlier ones.
+        int done = 0;
 #pragma unroll
-        for (int v = 0; v < kSelWaves; ++v) {
-            const int sv = scan_scratch[v];
-            pos += (v < w) ? sv : 0;
-            total += sv;
+        for (int rd = 0; rd < kRounds; ++rd) {
+            const int t = tid + kSelThreads * rd;
+            const bool c = t < N && state[t] == 0;
+            const uint64_t m = __ballot(c);
+            const int below = __builtin_amdgcn_mbcnt_hi(
+                static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+            if (lane == 0) scan_scratch[w] = __popcll(m);
+            __syncthreads();
+            int pos = done + below, total = 0;
+#pragma unroll
+            for (int v = 0; v < kSelWaves; ++v) {
+                const int sv = scan_scratch[v];
+                pos += (v < w) ? sv : 0;
+                total += sv;
+            }
+            if (c && pos < ld_cached) crow[pos] = t;
+            done += total;
+            __syncthreads();  // every wave has read scan_scratch before the next round writes it
         }
-        if (c && pos < ld_cached) crow[pos] = tid;
-        for (int t = total + tid; t < ld_cached; t += kSelThreads) crow[t] = -1;
-        if (tid == 0) cached_len[b] = total;
+        for (int t = done + tid; t < ld_cached; t += kSelThreads) crow[t] = -1;
+        if (tid == 0) cached_len[b] = done;
         return;
     }
 
@@ -684,7 +701,10 @@ int launch_refresh_select(const float* workspace, const int32_t* gp_idx, int ld_
     hipLaunchKernelGGL(refresh_select_kernel<NB>, dim3(B), dim3(kSelThreads), lds2, stream,     \
                        workspace, gp_idx, ld_gp, n_gp, K, inv_hg, scores, active_idx, ld_act,   \
                        cached_idx, ld_cached, cached_len, H, N)
-    switch ((N + kWave - 1) / kWave) {
+    // one instantiation per block count up to 8, then a few sizes up to 32
+    // (blocks past N hold key 0 and count nothing)
+    const int nb = (N + kWave - 1) / kWave;
+    switch (nb) {
         case 1: MARCA_SELECT(1); break;
         case 2: MARCA_SELECT(2); break;
         case 3: MARCA_SELECT(3); break;
@@ -693,7 +713,14 @@ int launch_refresh_select(const float* workspace, const int32_t* gp_idx, int ld_
         case 6: MARCA_SELECT(6); break;
         case 7: MARCA_SELECT(7); break;
         case 8: MARCA_SELECT(8); break;
-        default: MARCA_SELECT(0); break;
+        default:
+            if (nb <= 12) MARCA_SELECT(12);
+            else if (nb <= 16) MARCA_SELECT(16);
+            else if (nb <= 18) MARCA_SELECT(18);
+            else if (nb <= 24) MARCA_SELECT(24);
+            else if (nb <= kSelMaxRegBlocks) MARCA_SELECT(32);
+            else MARCA_SELECT(0);
+            break;
     }
 #undef MARCA_SELECT
     return status_from_launch();

@@ -129,9 +129,13 @@ def check_topk(q, k, gp, scores, act, cac, clen, K):
     (2, 2, 26, 1088, 52, 76, "bf16"), (1, 2, 64, 200, 10, 20, "bf16"),
     (1, 2, 64, 300, 10, 20, "bf16"),
     # the register-resident scores take up to 16 queries and 320 keys; the
-    # selection keeps up to 512 keys in registers, past that it reads LDS
+    # selection keeps up to 2048 keys in registers (one round of one token per
+    # thread up to 1024, two rounds up to 2048), past that it reads LDS
     (2, 2, 16, 319, 32, 16, "bf16"), (2, 2, 16, 321, 32, 16, "bf16"),
     (2, 2, 16, 500, 40, 25, "bf16"), (2, 2, 12, 700, 30, 40, "bf16"),
+    (1, 2, 16, 1024, 20, 30, "bf16"), (1, 2, 16, 1025, 20, 30, "bf16"),
+    (1, 2, 16, 1500, 40, 30, "bf16"), (1, 2, 16, 2048, 40, 30, "bf16"),
+    (1, 2, 16, 2500, 40, 30, "bf16"),
     # one token (every other key of the only tile masked; its score is 1) and one
     # token past a whole tile
     (1, 2, 4, 1, 0, 1, "bf16"), (2, 2, 16, 17, 0, 5, "bf16")])
