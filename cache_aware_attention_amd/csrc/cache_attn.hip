@@ -10,7 +10,7 @@
 // at each chunk boundary (the active/cached boundary among them) the state is
 // rescaled by 2^(m_old - m_new), which is the same merge rule.
 //
-// Four code paths:
+// Five code paths:
 //  * attn_mfma_kernel (bf16, A >= 16): one wave per (sequence, head) unit and
 //    query group of up to 64 queries.  S^T = K Q^T and O^T = V^T P^T run on
 //    v_mfma_f32_16x16x32_bf16; K goes straight from HBM into MFMA operand
@@ -33,8 +33,12 @@
 //    80 queries with the same per-chunk math, whose chunk stream runs on from
 //    one (unit, query block) item to the next together with the next item's
 //    queries.
-//  * attn_unit_kernel (fp32 any A, bf16 A < 16): a workgroup per unit and
-//    block of 64 queries streams 64-row K/V chunks through LDS; fp32 FMAs.
+//  * attn_f32_mfma_kernel (fp32, A >= 16): one wave per unit and query group,
+//    S^T and O^T on v_mfma_f32_16x16x4_f32 with every operand loaded from
+//    memory straight into the layout the products take (no LDS tile).
+//  * attn_unit_kernel (fp32 below 16 queries or past 8192 tokens, bf16 below
+//    16 queries): a workgroup per unit and block of 64 queries streams 64-row
+//    K/V chunks through LDS; fp32 FMAs.
 //
 // Head dim is fixed at 64 (MAR-B/L/H all use 64).  The cached index list is
 // sanitised: an entry outside [0, N) is skipped, never dereferenced.  Inputs
@@ -53,8 +57,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
-// Per-unit vector path (fp32 inputs at any A; bf16 below 16 active queries,
-// where a 16-wide MFMA tile would be mostly empty): fp32 FMAs throughout.
+// Per-unit vector path (fp32 inputs below 16 active queries or past 8192
+// tokens; bf16 below 16 active queries, where a 16-wide MFMA tile would be
+// mostly empty): fp32 FMAs throughout.
 //
 // A workgroup of 4 waves per (sequence, head) unit and block of 64 queries
 // streams the unit's virtual sequence [active rows ; cached rows] in chunks
@@ -836,6 +841,270 @@ void attn_mfma_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restri
         if (row < nq) {
             const u32x4_t w = *reinterpret_cast<const u32x4_t*>(tile + swz(row, lane & 7));
             __builtin_nontemporal_store(w, orow + row * 8 + (lane & 7));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 matrix-core path (fp32 inputs, A >= 16): one wave per (sequence, head)
+// unit and group of up to 16*NQT queries, as attn_mfma_kernel, on
+// v_mfma_f32_16x16x4_f32 (lane l supplies A[l%16][l/16] and B[l/16][l%16];
+// the output has lane l holding rows 4(l/16)..4(l/16)+3 of column l%16).
+// Which head dims or keys a product's four k-slots take, and which dims its
+// output rows stand for, is free as long as the operands agree, so every
+// operand comes from memory already in place and there is no LDS tile:
+//  * S^T = K Q^T over 16-key chunks, in 16 steps: step 4j + e gives lane
+//    (g, m) head dim 16j + 4g + e of key row m and of query m.  Load j of a
+//    lane is floats [16j + 4g, +4) of its row, so one load instruction reads
+//    64 contiguous bytes of each of 16 rows.  The output gives lane (g, m) the
+//    scores of keys 4g..4g+3 against query m.
+//  * O^T = V^T P^T, per 16-dim output tile dt, in 4 steps: step s gives lane
+//    (g, m) key 4g + s, i.e. its own probability p[s] as the B operand and
+//    V[key 4g+s][dim pi(dt, m)] as the A operand, with output row i of tile
+//    dt standing for dim pi(dt, i) = 16(i % 4) + 4(i / 4) + dt.  A lane loads
+//    V rows 4g..4g+3 at floats [16(m % 4) + 4(m / 4), +4) (16 lanes read each
+//    whole row) and ends holding O[m][16r + 4g + dt] = oacc[dt][r], stored
+//    with one instruction per r writing 64 contiguous bytes of 16 rows.
+// The softmax state follows attn_mfma_kernel (a reference maximum per query,
+// the state rescaled when a chunk's maximum passes it by kRescaleLog2); the
+// probabilities stay in fp32, and each lane keeps the row sum over its own
+// keys, summed over the four lane groups at the end.  The cached list is
+// staged in LDS; missing rows read active row 0 and are masked.
+// ---------------------------------------------------------------------------
+constexpr int kF32Chunk = 16;  // key rows per chunk
+
+// Sum over lanes l, l^16, l^32, l^48 (register-only lane swaps).
+__device__ __forceinline__ float sum_over_groups(float x) {
+    const uint32_t u = __float_as_uint(x);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t v = __float_as_uint(x);
+    auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Registers of one fp32 chunk in flight: K floats [16j + 4g, +4) of key row m
+// (j < 4), V floats [16(m % 4) + 4(m / 4), +4) of key rows 4g+s, and the
+// chunk's row mask.
+struct F32Chunk {
+    float4 k[4];
+    float4 v[4];
+    uint32_t valid;  // bit j: key row j of the chunk exists (wave-uniform)
+};
+
+template <int NQT, bool RAGGED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void attn_f32_mfma_kernel(const float* __restrict__ q_a, const float* __restrict__ k_a,
+                          const float* __restrict__ v_a, const float* __restrict__ k_cache,
+                          const float* __restrict__ v_cache, const int32_t* __restrict__ cached_idx,
+                          int ldc, float* __restrict__ out, float* __restrict__ lse, int units,
+                          int H, int N, int A, int Nc, int n_groups, float scale_log2,
+                          const int32_t* __restrict__ a_len, const int32_t* __restrict__ c_len) {
+    constexpr int kPF = (NQT <= 3) ? 2 : 1;  // chunks in flight
+    extern __shared__ __align__(16) int32_t f32_cidx_s[];  // [max(Nc, 1)]
+    const int lane = threadIdx.x;
+    const int g = lane >> 4;
+    const int m = lane & 15;
+
+    // The query groups of one unit sit on one XCD (workgroups go round-robin
+    // over the 8), so the later groups' K/V reads hit that XCD's L2.
+    int u, qg;
+    if (n_groups == 1) {
+        u = blockIdx.x;
+        qg = 0;
+    } else {
+        const int xcd = blockIdx.x & 7;
+        const int slot = blockIdx.x >> 3;
+        u = (slot / n_groups) * 8 + xcd;
+        qg = slot % n_groups;
+        if (u >= units) return;  // uniform (one-wave workgroup)
+    }
+    const int b = u / H;
+    int An = A, Ncn = Nc;
+    if constexpr (RAGGED) {
+        An = min(max(a_len[b], 0), A);
+        Ncn = min(max(c_len[b], 0), Nc);
+    }
+    const int q0 = qg * kQueriesPerGroup;
+    if (q0 >= An) return;  // no queries in this group (uniform; RAGGED only)
+    const int nq = min(An - q0, 16 * NQT);
+
+    const float* ka_u = k_a + static_cast<size_t>(u) * A * kD;
+    const float* va_u = v_a + static_cast<size_t>(u) * A * kD;
+    const float* kc_u = k_cache + static_cast<size_t>(u) * N * kD;
+    const float* vc_u = v_cache + static_cast<size_t>(u) * N * kD;
+    const int T = An + Ncn;
+    const int nchunks = (T + kF32Chunk - 1) / kF32Chunk;
+
+    // The list's first entries are requested before the queries.
+    constexpr int kIdxRegs = 8;
+    const int32_t* cidx_g = cached_idx + static_cast<size_t>(b) * ldc;
+    int32_t iv[kIdxRegs];
+#pragma unroll
+    for (int k = 0; k < kIdxRegs; ++k) {
+        const int c = lane + kWave * k;
+        iv[k] = (c < Ncn) ? cidx_g[c] : -1;
+    }
+    // Query operands: lane (g, m) holds floats [16j + 4g, +4) (j < 4) of
+    // query 16qt + m (past the group's end: its last query, never stored).
+    float4 qv[NQT][4];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        const int qi = q0 + min(16 * qt + m, nq - 1);
+        const float4* qp = reinterpret_cast<const float4*>(q_a + (static_cast<size_t>(u) * A + qi) * kD);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qv[qt][j] = ld_stream(qp + 4 * j + g);
+    }
+    // Stage the cached list (entries outside [0, N) become -1).
+#pragma unroll
+    for (int k = 0; k < kIdxRegs; ++k) {
+        const int c = lane + kWave * k;
+        if (c < Ncn) f32_cidx_s[c] = (iv[k] >= 0 && iv[k] < N) ? iv[k] : -1;
+    }
+    for (int c = lane + kWave * kIdxRegs; c < Ncn; c += kWave) {
+        const int n = cidx_g[c];
+        f32_cidx_s[c] = (n >= 0 && n < N) ? n : -1;
+    }
+    __syncthreads();  // one wave: orders the list writes before the reads
+
+    auto issue = [&](int c, F32Chunk& cr) __attribute__((always_inline)) {
+        const int r0 = c * kF32Chunk;
+        bool is_c, ok;
+        const int ko = row_ofs(r0 + m, An, Ncn, f32_cidx_s, is_c, ok) + 4 * g;
+        cr.valid = static_cast<uint32_t>(__ballot(ok) & 0xffffull);
+        const float4* kp = reinterpret_cast<const float4*>((is_c ? kc_u : ka_u) + ko);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cr.k[j] = ld_stream(kp + 4 * j);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bool vc, vok;
+            const int vo = row_ofs(r0 + 4 * g + s, An, Ncn, f32_cidx_s, vc, vok) + 16 * (m & 3) + 4 * (m >> 2);
+            cr.v[s] = ld_stream(reinterpret_cast<const float4*>((vc ? vc_u : va_u) + vo));
+        }
+    };
+
+    const float thr_raw = kRescaleLog2 / scale_log2;
+    float mref[NQT], mc[NQT], mthr[NQT], lsum[NQT];
+    f32x4_t oacc[NQT][4];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        mref[qt] = -INFINITY;
+        mthr[qt] = -INFINITY;
+        mc[qt] = 0.f;
+        lsum[qt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    auto f4 = [](const float4& x, int j) __attribute__((always_inline)) {
+        return j == 0 ? x.x : (j == 1 ? x.y : (j == 2 ? x.z : x.w));
+    };
+
+    auto compute = [&](const F32Chunk& ch) __attribute__((always_inline)) {
+        // S^T tiles of all query tiles, step by step (NQT independent chains).
+        f32x4_t sc[NQT];
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) sc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+                sc[qt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4(ch.k[s >> 2], s & 3),
+                                                              f4(qv[qt][s >> 2], s & 3), sc[qt], 0,
+                                                              0, 0);
+        // Masking, then every tile's probabilities against its current
+        // reference before the one rescale test of the chunk, which only
+        // decides whether they are taken again (rare).  Tiles past the
+        // group's queries repeat its last query and are never stored; they
+        // are computed too, so the chunk stays one basic block.
+        if (ch.valid != 0xffffu) {  // wave-uniform
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!((ch.valid >> (4 * g + i)) & 1u)) sc[qt][i] = -INFINITY;
+        }
+        float mx[NQT], p[NQT][4];
+        bool up = false;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            mx[qt] = fmaxf(fmaxf(sc[qt][0], sc[qt][1]), fmaxf(sc[qt][2], sc[qt][3]));
+            up = up || (mx[qt] > mthr[qt]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p[qt][i] = __builtin_amdgcn_exp2f(fmaf(sc[qt][i], scale_log2, -mc[qt]));
+        }
+        if (__builtin_expect(__any(up), 0)) {  // a query's maximum moved far up: rescale
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const float mnew = fmaxf(mref[qt], max_over_groups(mx[qt]));
+                if (mnew > mthr[qt] || mref[qt] == -INFINITY) {
+                    const float alpha = (mref[qt] == -INFINITY)
+                                            ? 0.f
+                                            : __builtin_amdgcn_exp2f((mref[qt] - mnew) * scale_log2);
+                    lsum[qt] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] *= alpha;
+                    mref[qt] = mnew;
+                    mc[qt] = mnew * scale_log2;
+                    mthr[qt] = mnew + thr_raw;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        p[qt][i] = __builtin_amdgcn_exp2f(fmaf(sc[qt][i], scale_log2, -mc[qt]));
+                }
+            }
+        }
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            lsum[qt] += (p[qt][0] + p[qt][1]) + (p[qt][2] + p[qt][3]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4(ch.v[s], dt), p[qt][s],
+                                                                       oacc[qt][dt], 0, 0, 0);
+        }
+    };
+
+    // Chunk c lives in cr[c % (kPF + 1)]; each step requests chunk c + kPF
+    // (past the end: rows that do not exist, which read active row 0) and
+    // computes chunk c, so every step issues the same loads.
+    F32Chunk cr[kPF + 1];
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) issue(k, cr[k]);
+    auto step = [&](int c, auto buf_tag) __attribute__((always_inline)) {
+        constexpr int BI = decltype(buf_tag)::value;
+        constexpr int BN = (BI + kPF) % (kPF + 1);
+        issue(c + kPF, cr[BN]);
+        compute(cr[BI]);
+    };
+    int c = 0;
+    for (; c + kPF < nchunks; c += kPF + 1) {
+        step(c, std::integral_constant<int, 0>{});
+        step(c + 1, std::integral_constant<int, 1>{});
+        if constexpr (kPF >= 2) step(c + 2, std::integral_constant<int, 2>{});
+    }
+    if (c < nchunks) step(c, std::integral_constant<int, 0>{});
+    if constexpr (kPF >= 2)
+        if (c + 1 < nchunks) step(c + 1, std::integral_constant<int, 1>{});
+
+    // Finalise: lane (g, m) writes dims [16r + 4g, +4) (r < 4) of query 16qt + m.
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        const int row = 16 * qt + m;
+        if (16 * qt >= nq) continue;  // wave-uniform
+        const float l = sum_over_groups(lsum[qt]);
+        const float inv = 1.f / l;
+        if (row < nq) {
+            float4* orow = reinterpret_cast<float4*>(out + (static_cast<size_t>(u) * A + q0 + row) * kD + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float4 w = make_float4(oacc[qt][0][r] * inv, oacc[qt][1][r] * inv,
+                                             oacc[qt][2][r] * inv, oacc[qt][3][r] * inv);
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, w),
+                                            reinterpret_cast<u32x4_t*>(orow + 4 * r));
+            }
+            if (lse != nullptr && g == 0)
+                lse[static_cast<size_t>(u) * A + q0 + row] = (mc[qt] + log2f(l)) * kLn2;
         }
     }
 }
@@ -1970,6 +2239,37 @@ int dispatch_mfma(const uint16_t* q, const uint16_t* ka, const uint16_t* va, con
 
 namespace {
 
+// fp32 inputs, A >= 16: attn_f32_mfma_kernel, one wave per (unit, group of up
+// to 64 queries), the groups of a unit on one XCD.
+int launch_f32_mfma(const float* q_a, const float* k_a, const float* v_a, const float* k_cache,
+                    const float* v_cache, const int32_t* cached_idx, int ldc, float* out,
+                    float* lse, int B, int H, int N, int A, int Nc, float scale_log2,
+                    const int32_t* a_len, const int32_t* c_len, hipStream_t stream) {
+    const int units = B * H;
+    const int n_groups = (A + kQueriesPerGroup - 1) / kQueriesPerGroup;
+    const int grid = (n_groups == 1) ? units : ((units + 7) / 8) * 8 * n_groups;
+    const size_t lds = static_cast<size_t>(Nc > 0 ? Nc : 1) * 4;
+    const int nqt = (n_groups > 1) ? 4 : (A + 15) / 16;
+    auto go = [&](auto nqt_tag) {
+        constexpr int kNqt = decltype(nqt_tag)::value;
+        if (a_len != nullptr)
+            hipLaunchKernelGGL((attn_f32_mfma_kernel<kNqt, true>), dim3(grid), dim3(64), lds,
+                               stream, q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
+                               units, H, N, A, Nc, n_groups, scale_log2, a_len, c_len);
+        else
+            hipLaunchKernelGGL((attn_f32_mfma_kernel<kNqt, false>), dim3(grid), dim3(64), lds,
+                               stream, q_a, k_a, v_a, k_cache, v_cache, cached_idx, ldc, out, lse,
+                               units, H, N, A, Nc, n_groups, scale_log2, a_len, c_len);
+        return status_from_launch();
+    };
+    switch (nqt) {
+        case 1: return go(std::integral_constant<int, 1>{});
+        case 2: return go(std::integral_constant<int, 2>{});
+        case 3: return go(std::integral_constant<int, 3>{});
+        default: return go(std::integral_constant<int, 4>{});
+    }
+}
+
 int launch_attn_impl(const void* q_a, const void* k_a, const void* v_a, const void* k_cache,
                      const void* v_cache, const int32_t* cached_idx, int ldc, void* out,
                      float* lse, int B, int H, int N, int A, int Nc, float scale, int dtype,
@@ -1987,6 +2287,12 @@ int launch_attn_impl(const void* q_a, const void* k_a, const void* v_a, const vo
         return dispatch_mfma<false>(q, ka, va, kc, vc, cached_idx, ldc, o, lse, B, H, N, A, Nc,
                                     scale_log2, nullptr, 0, nullptr, a_len, c_len, stream);
     }
+    if (dtype == MAR_F32 && A >= 16 && N <= kMaxMfmaTokens)
+        return launch_f32_mfma(static_cast<const float*>(q_a), static_cast<const float*>(k_a),
+                               static_cast<const float*>(v_a), static_cast<const float*>(k_cache),
+                               static_cast<const float*>(v_cache), cached_idx, ldc,
+                               static_cast<float*>(out), lse, B, H, N, A, Nc, scale_log2, a_len,
+                               c_len, static_cast<hipStream_t>(stream_v));
     const dim3 grid(B * H, (A + kUnitQ - 1) / kUnitQ);
     if (dtype == MAR_BF16) {
         hipLaunchKernelGGL(attn_unit_kernel<uint16_t>, grid, dim3(256), 0, stream,
