@@ -11,8 +11,9 @@ Covered: the query tile counts 1-4 and two query groups, partial last tiles
 and chunks, an empty and a one-entry cached list, invalid list entries, the
 softmax rescale path (scores that climb along the sequence), per-sequence
 counts (including sequences with no queries, left untouched), the fused cache
-update (attention + row scatter, same output bits), and the MAR-L shape at
-full size on sampled units.
+update (attention + row scatter, same output bits), the longest sequence the
+path takes (8192 tokens) and one past it, an all-invalid list, and the MAR-L
+shape at full size on sampled units.
 """
 import numpy as np
 import pytest
@@ -179,3 +180,34 @@ def test_f32_full_size_mar_l_sampled(marca):
         o, l = oracle_unit(x["q_a"], x["k_a"], x["v_a"], x["k_cache"], x["v_cache"], x["cached"],
                            b, h, A, cfg.Nc)
         check_unit(out[b, h], lse[b, h], o, l, (b, h))
+
+
+@pytest.mark.parametrize("N,A", [(8192, 32), (8193, 32)])
+def test_f32_longest_sequences(marca, N, A):
+    """The largest token count the fp32 matrix-core path takes (a 32 KB staged
+    list) and one past it, where the per-unit vector path takes over."""
+    cfg = small_cfg(B=1, H=2, N=N, A=A, seed=7500 + N)
+    x = attention_inputs(cfg, DEV, ascending=False)
+    lse = torch.empty((1, 2, A), dtype=torch.float32, device=DEV)
+    out = marca.mar_cache_attn_fwd(x["q_a"], x["k_a"], x["v_a"], x["k_cache"], x["v_cache"],
+                                   x["cached"], Nc=N - A, lse=lse)
+    torch.cuda.synchronize()
+    for h in range(2):
+        o, l = oracle_unit(x["q_a"], x["k_a"], x["v_a"], x["k_cache"], x["v_cache"], x["cached"],
+                           0, h, A, N - A)
+        check_unit(out[0, h], lse[0, h], o, l, (N, h))
+
+
+def test_f32_all_cached_entries_invalid(marca):
+    """Every list entry is out of range: the same bits as attention over the
+    active rows alone."""
+    cfg = small_cfg(B=2, H=2, N=200, A=48, seed=7600)
+    x = attention_inputs(cfg, DEV)
+    bad = torch.full((2, 152), -1, dtype=torch.int32, device=DEV)
+    bad[:, ::3] = 200 + 7
+    out = marca.mar_cache_attn_fwd(x["q_a"], x["k_a"], x["v_a"], x["k_cache"], x["v_cache"], bad,
+                                   Nc=152)
+    ref = marca.mar_cache_attn_fwd(x["q_a"], x["k_a"], x["v_a"], x["k_cache"], x["v_cache"], None,
+                                   Nc=0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
