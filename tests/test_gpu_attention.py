@@ -121,7 +121,9 @@ def test_bf16_mfma_path_ragged(marca, A, Nc):
 
 @pytest.mark.parametrize("dtype,A", [("bf16", 1), ("bf16", 5), ("bf16", 15), ("f32", 1),
                                      ("f32", 8), ("f32", 33), ("f32", 70)])
-def test_rowwise_path(marca, dtype, A):
+def test_vector_and_fp32_paths(marca, dtype, A):
+    """Below 16 active queries (bf16 and fp32) the per-unit vector kernel runs;
+    fp32 with 16 or more the fp32 matrix-core kernel (one and two query groups)."""
     Nc = 150
     cfg = small_cfg(dtype, B=2, H=2, N=A + Nc, A=A, seed=500 + A)
     x = attention_inputs(cfg, DEV, ascending=False)
