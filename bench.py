@@ -647,6 +647,8 @@ def main():
                     help="only the locality comparison's kernels, a fixed sequence (counter runs)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the plain copy kernel (counter calibration)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="only the other configurations' calls (one JSON object; counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -690,6 +692,10 @@ def main():
             del layers
             torch.cuda.empty_cache()
         print(json.dumps({"dispatch_order": order}))
+        return
+
+    if args.configs_only:
+        print(json.dumps(other_configs(marca, dev, torch.cuda.current_stream())))
         return
 
     if args.copy_only:
