@@ -181,3 +181,55 @@ def test_ragged_update(marca, B, H, A, Nc):
                           torch.from_numpy(v0).view(torch.bfloat16).to(DEV), cached_d, b, b % H,
                           an, cn, D ** -0.5)
         assert np.abs(f64(out[b, b % H, :an]) - o).max() <= 2e-2, b
+
+
+def test_ragged_update_full_size_gated_layer(marca):
+    """A high-res gated layer at full size, as the high-res decode runs it: 64
+    sequences x 16 heads x 1088 tokens, the token gate (W = 1024, 0.95) picks
+    each sequence's tokens to recompute, and mar_cache_attn_fwd_ragged_update
+    attends their fresh rows over the cached rows of the reused tokens and
+    writes the fresh rows into the caches.  Checked: the output equals
+    mar_cache_attn_fwd_ragged's bit for bit, every recomputed row of every
+    head is written and no other row changes (sampled sequences), and sampled
+    (sequence, head) units match the oracle."""
+    from mar_workloads import device_gate_features
+    B, H, N, D, W = 64, 16, 1088, 64, 1024
+    gx, gy, _ = device_gate_features(B, N, W, seed=77, device=DEV)
+    reuse_idx = torch.empty((B, N), dtype=torch.int32, device=DEV)
+    reuse_len = torch.empty((B,), dtype=torch.int32, device=DEV)
+    _, _, comp, clen = marca.mar_cos_gate(gx, gy, 0.95, reuse_idx=reuse_idx, reuse_len=reuse_len)
+    del gx, gy
+    torch.cuda.synchronize()
+    a_cap = int(clen.max())
+    nc_cap = int(reuse_len.max())
+    assert 100 < a_cap < N and ((clen + reuse_len) == N).all()
+    qf, kf, vf = (device_normal((B, H, N, D), 60 + i, DEV, torch.bfloat16) for i in range(3))
+    kc, vc = (device_normal((B, H, N, D), 70 + i, DEV, torch.bfloat16) for i in range(2))
+    pos = comp[:, :a_cap].clamp(min=0).long()
+    gat = lambda x: torch.gather(x, 2, pos[:, None, :, None].expand(B, H, a_cap, D)).contiguous()
+    q_a, k_a, v_a = gat(qf), gat(kf), gat(vf)
+    del qf, kf, vf
+    active = comp[:, :a_cap].contiguous()
+    cached = reuse_idx[:, :nc_cap].contiguous()
+    ref = marca.mar_cache_attn_fwd_ragged(q_a, k_a, v_a, kc, vc, cached, clen, reuse_len)
+    torch.cuda.synchronize()
+    samples = (0, 17, 40, B - 1)
+    before_k = {b: kc[b].clone() for b in samples}
+    before_v = {b: vc[b].clone() for b in samples}
+    out = marca.mar_cache_attn_fwd_ragged_update(q_a, k_a, v_a, kc, vc, cached, active, clen,
+                                                 reuse_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    for b in samples:
+        an = int(clen[b])
+        rows = comp[b, :an].long()
+        assert torch.equal(kc[b][:, rows], k_a[b, :, :an]) and torch.equal(vc[b][:, rows], v_a[b, :, :an])
+        keep = torch.ones(N, dtype=torch.bool, device=DEV)
+        keep[rows] = False
+        assert torch.equal(kc[b][:, keep], before_k[b][:, keep])
+        assert torch.equal(vc[b][:, keep], before_v[b][:, keep])
+    for b, h in ((0, 0), (17, 5), (40, 15), (B - 1, 9)):
+        an, cn = int(clen[b]), int(reuse_len[b])
+        o, _ = oracle_seq(q_a, k_a, v_a, before_k[b][None].expand(B, H, N, D),
+                          before_v[b][None].expand(B, H, N, D), cached, b, h, an, cn, D ** -0.5)
+        assert np.abs(f64(out[b, h, :an]) - o).max() <= 2e-2, (b, h)
