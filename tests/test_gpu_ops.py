@@ -193,6 +193,30 @@ def test_topk_full_size_mar_l(marca):
         assert (np.diff(c[b, :L[b]]) > 0).all()
 
 
+def test_topk_full_size_highres(marca):
+    """High-res: 64 sequences, 16 heads, 26 generating queries, N 1088, |G|+|P| =
+    52, K 76 (a budget of 128), as the high-res decode's layer 2 calls it:
+    sampled sequences against the oracle, properties on all of them."""
+    cfg = CONFIGS["highres"]
+    order = torch.from_numpy(generation_order(cfg)).to(DEV)
+    gp = order[:, 300:352]
+    q = device_normal((cfg.B, cfg.H, 26, 64), 13, DEV, torch.bfloat16)
+    k = device_normal((cfg.B, cfg.H, cfg.N, 64), 14, DEV, torch.bfloat16)
+    scores, act, cac, clen = marca.mar_refresh_topk(q, k, gp, 52, 76)
+    torch.cuda.synchronize()
+    rows = [0, 21, 42, 63]
+    check_topk(q[rows], k[rows], gp[rows].contiguous(), scores[rows], act[rows], cac[rows],
+               clen[rows], 76)
+    assert torch.allclose(scores.sum(1), torch.ones(cfg.B, device=DEV), atol=1e-4)
+    a = act.cpu().numpy()
+    c = cac.cpu().numpy()
+    L = clen.cpu().numpy()
+    for b in range(cfg.B):
+        allv = np.concatenate([a[b], c[b, :L[b]]])
+        assert sorted(allv.tolist()) == list(range(cfg.N))
+        assert (np.diff(c[b, :L[b]]) > 0).all()
+
+
 # ---------------------------------------------------------------- gate -----
 
 # Both sides reduce the same input values (a bf16 product is exact in fp32):
