@@ -1061,11 +1061,22 @@ def main():
     except Exception as exc:  # noqa: BLE001 - reported, not fatal
         print(f"bench: copy measurement failed: {exc}", file=sys.stderr)
 
-    configs = None if args.no_decode else other_configs(marca, dev, stream)
-    loc = None if args.no_decode else locality(marca, dev, stream)
+    def optional(name, fn):
+        # a leg outside the headline that raises is reported in its own field
+        # (and on stderr) instead of taking the headline record down with it
+        try:
+            return fn()
+        except Exception as exc:  # noqa: BLE001 - reported in the record
+            print(f"bench: {name} failed: {exc!r}", file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+            return {"error": repr(exc)}
+
+    configs = None if args.no_decode else optional(
+        "configs", lambda: other_configs(marca, dev, stream))
+    loc = None if args.no_decode else optional("locality", lambda: locality(marca, dev, stream))
     if not args.no_decode:
         print("bench: high-res 64-step decode", file=sys.stderr, flush=True)
-    c5 = None if args.no_decode else c5_decode(marca, dev, stream)
+    c5 = None if args.no_decode else optional("c5_decode", lambda: c5_decode(marca, dev, stream))
 
     cpu = None
     if not args.no_cpu_baseline:
