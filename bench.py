@@ -1068,7 +1068,6 @@ def main():
             return fn()
         except Exception as exc:  # noqa: BLE001 - reported in the record
             print(f"bench: {name} failed: {exc!r}", file=sys.stderr, flush=True)
-            torch.cuda.synchronize()
             return {"error": repr(exc)}
 
     configs = None if args.no_decode else optional(
