@@ -1087,8 +1087,25 @@ def main():
     line["roofline"].update({"kernel": "mar_cache_attn_fwd_update (attention + cache update)",
                              "bytes_per_call": bytes_fused,
                              "us_per_call": avg_us["attn_update"]})
+    def hbm_rate(us, nbytes):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us_per_call": us, "bytes_per_call": nbytes, "gbs": gbs,
+                "frac_hbm": gbs / PEAK_HBM_GBS}
+
+    B_, H_, N_, D_ = cfg.B, cfg.H, cfg.N, cfg.D
     line.update({
         "kernel_us": avg_us,
+        "step_kernels": {
+            "what": "the step's other kernels against 8 TB/s, algorithmic bytes per call: the "
+                    "top-K reads the generating queries and layer 2's K and writes the scores "
+                    "and the partition, the scatter reads and writes the active rows, the gate "
+                    "reads both feature sets and writes cosines, mask and list; the CFG residual "
+                    "(about 3 MB) is reported in microseconds only",
+            "topk": hbm_rate(avg_us["topk"], B_ * H_ * (cfg.n_gen + N_) * D_ * 2 + B_ * N_ * 5
+                             + B_ * (cfg.K + cfg.Nc) * 4),
+            "scatter": hbm_rate(avg_us["scatter"], 4 * B_ * H_ * cfg.A * D_ * 2),
+            "gate": hbm_rate(avg_us["gate"], 2 * B_ * N_ * cfg.W * 2 + B_ * N_ * 9),
+            "cfg_us_per_call": avg_us["cfg"]},
         "attention_roofline": {
             "what": "the cache-aware attention alone (mar_cache_attn_fwd), same layers",
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
