@@ -442,6 +442,24 @@ __global__ __launch_bounds__(64 * W) void refresh_scores_reg_kernel(
     }
 }
 
+// Token j's partials summed over the H heads in head order, with the loads of
+// a batch of heads issued together (a loop of dependent load-add steps would
+// wait for each load in turn).
+__device__ __forceinline__ float head_sum(const float* __restrict__ ws, int b, int H, int N, int j) {
+    constexpr int kBatch = 16;
+    float s = 0.f;
+    for (int h0 = 0; h0 < H; h0 += kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            v[i] = (h0 + i < H) ? ws[((size_t)b * H + h0 + i) * N + j] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (h0 + i < H) s += v[i];
+    }
+    return s;
+}
+
 __device__ __forceinline__ uint64_t rank_key(float s, int j) {
     const uint32_t u = __float_as_uint(s);
     const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -487,9 +505,7 @@ __global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
     // first token) are issued before the first barrier so their latencies
     // overlap.
     const int gp0 = (tid < n_gp) ? gp_idx[(size_t)b * ld_gp + tid] : -1;
-    float s0 = 0.f;
-    if (tid < N)
-        for (int h = 0; h < H; ++h) s0 += ws[((size_t)b * H + h) * N + tid];  // fixed order
+    const float s0 = (tid < N) ? head_sum(ws, b, H, N, tid) : 0.f;  // fixed order
     for (int j = tid; j < N; j += kSelThreads) state[j] = 0;
     for (int r = tid; r < K; r += kSelThreads) arow[n_gp + r] = -1;  // fewer eligible than K
     __syncthreads();
@@ -500,11 +516,7 @@ __global__ __launch_bounds__(kSelThreads) void refresh_select_kernel(
     }
     __syncthreads();
     for (int j = tid; j < N; j += kSelThreads) {
-        float s = s0;
-        if (j != tid) {
-            s = 0.f;
-            for (int h = 0; h < H; ++h) s += ws[((size_t)b * H + h) * N + j];
-        }
+        float s = (j != tid) ? head_sum(ws, b, H, N, j) : s0;
         s *= inv_hg;
         scores[(size_t)b * N + j] = s;
         keys[j] = (state[j] == 0) ? rank_key(s, j) : 0ull;
