@@ -45,7 +45,9 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mar_l_traffic.json")
 DECODE_ROUNDS = 3
-ATTN_SRC = os.path.join(ROOT, "cache_aware_attention_amd", "csrc", "cache_attn.hip")
+# The attention kernels' sources: the counter record is valid for these bytes only.
+ATTN_SRC = tuple(os.path.join(ROOT, "cache_aware_attention_amd", "csrc", f)
+                 for f in ("cache_attn.hip", "attn_dense.h"))
 
 
 def attn_bytes(B, H, A, Nc, D, elem=2):
@@ -105,9 +107,13 @@ def roofline_for(flops, nbytes, seconds):
     return r
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    """sha256 (first 16 hex digits) of one file, or of several files' bytes in order."""
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kind):
@@ -934,6 +940,14 @@ def main():
                  L["v_a"], L["k_cache"], L["v_cache"], x["cached_idx"], cfg.Nc, L["out"],
                  write_out=write_out, stream=stream)()
 
+    def full_floor(l, mode):
+        """The full-attention kernel on layer l's buffers (as full_attn) in a
+        measurement mode: its arithmetic alone or its memory operations alone."""
+        x = X[0]
+        L, Lq = x["layers"][l], x["layers"][(l + n_ca // 2) % n_ca]
+        prepared(("full_floor", l, mode), _bench_lib.mar_bench_dense_floor, Lq["k_cache"],
+                 L["k_cache"], L["v_cache"], x["full_out"], mode, stream=stream)()
+
     def timed_kernels():
         """The same launches as one step, grouped by kernel so that one pair of HIP
         events brackets each group of back-to-back launches (an event pair around
@@ -953,6 +967,10 @@ def main():
         span("gate", gate, 1)
         span("full_attn", lambda: [full_attn(l) for l in range(n_ca)], n_ca)
         span("full_refresh", lambda: [full_refresh(l) for l in range(n_ca)], n_ca)
+        span("full_arith_only", lambda: [full_floor(l, _bench_lib.MAR_BENCH_FLOOR_ARITH)
+                                         for l in range(n_ca)], n_ca)
+        span("full_memory_only", lambda: [full_floor(l, _bench_lib.MAR_BENCH_FLOOR_MEMORY)
+                                          for l in range(n_ca)], n_ca)
         span("attn_pattern", lambda: [pattern(l, True) for l in range(n_ca)], n_ca)
         span("attn_pattern_reads", lambda: [pattern(l, False) for l in range(n_ca)], n_ca)
         span("layer2_separate", lambda: [layer2_separate(l, plan) for l in range(n_ca)], n_ca)
@@ -1126,7 +1144,15 @@ def main():
             "roofline": roofline_for(full_flops, full_bytes, avg_us["full_attn"] * 1e-6),
             "tflops": full_tflops,
             "refresh_roofline": roofline_for(full_flops, full_bytes + 2 * full_bytes // 4,
-                                             avg_us["full_refresh"] * 1e-6)},
+                                             avg_us["full_refresh"] * 1e-6),
+            "floors": {
+                "what": "the same kernel on the same layers in its measurement modes "
+                        "(mar_bench_dense_floor): its arithmetic, LDS traffic and barriers "
+                        "alone (no memory traffic) and its memory operations alone (no "
+                        "per-chunk math); the layer cannot take less than the larger",
+                "arith_only_us": avg_us["full_arith_only"],
+                "memory_only_us": avg_us["full_memory_only"],
+                "memory_only_gbs": full_bytes / (avg_us["full_memory_only"] * 1e-6) / 1e9}},
         "decode": None if args.no_decode else {
             "what": "one 64-step decode of the attention path (every layer's attention, cache "
                     "writes, top-K, CFG and gate; no projections or MLPs), with the cache "

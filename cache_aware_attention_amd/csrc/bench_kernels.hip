@@ -16,16 +16,18 @@
 //    and the fresh keys and values; the Pith review page, figure 7: runtime of
 //    standard versus cache-aware attention).  Row r of the output is active
 //    row r for r < A and cached row cached_idx[r - A] after that.
+//  * the full-attention kernel of the decoding path (attn_dense.h) in its two
+//    measurement modes: its arithmetic alone (every global load past the
+//    buffer, no memory traffic, no output) and its memory operations alone
+//    (no per-chunk math): the two floors that bound the full-attention layer.
 #include <type_traits>
 
+#include "attn_dense.h"
 #include "device_util.h"
 #include "mar_bench.h"
 
 namespace marca {
 namespace {
-
-constexpr int kD = 64;
-constexpr int kChunk = 32;
 
 template <bool WRITE, int NQT>
 __global__ __launch_bounds__(64) void attn_pattern_kernel(
@@ -209,4 +211,27 @@ extern "C" int mar_bench_kv_concat(void* k_cat, void* v_cat, const void* k_a, co
                        static_cast<const uint4*>(v_cache), cached_idx, ldc, H, N, A, Nc, pieces,
                        total);
     return status_from_launch();
+}
+
+extern "C" int mar_bench_dense_floor(const void* q, const void* k, const void* v, void* out,
+                                     int mode, int B, int H, int N, int D, int dtype,
+                                     void* stream) {
+    using namespace marca;
+    if (!q || !k || !v || !out) return MAR_E_NULL;
+    if (dtype != MAR_BF16) return MAR_E_UNSUPPORTED;
+    if (B < 1 || H < 1 || N < 1) return MAR_E_SHAPE;
+    if (D != kD || N <= 64 || N > 8192) return MAR_E_UNSUPPORTED;
+    if (mode != MAR_BENCH_FLOOR_ARITH && mode != MAR_BENCH_FLOOR_MEMORY) return MAR_E_RANGE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MAR_E_RANGE;
+    auto qq = static_cast<const uint16_t*>(q);
+    auto kk = static_cast<const uint16_t*>(k);
+    auto vv = static_cast<const uint16_t*>(v);
+    auto o = static_cast<uint16_t*>(out);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale_log2 = 0.125f * 1.4426950408889634f;
+    if (mode == MAR_BENCH_FLOOR_ARITH)
+        return launch_dense_wg<false, kLabArith>(qq, kk, vv, nullptr, nullptr, o, nullptr, B, H, N,
+                                                 scale_log2, s);
+    return launch_dense_wg<false, kLabMemory>(qq, kk, vv, nullptr, nullptr, o, nullptr, B, H, N,
+                                              scale_log2, s);
 }

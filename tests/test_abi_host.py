@@ -46,7 +46,7 @@ def test_bench_library_exports_and_rejections():
     declares and refuses bad arguments before any GPU work."""
     from cache_aware_attention_amd import _bench_lib
     names = declared_functions(os.path.join(ROOT, "include", "mar_bench.h"))
-    assert names == ["mar_bench_attn_pattern", "mar_bench_kv_concat"]
+    assert names == ["mar_bench_attn_pattern", "mar_bench_dense_floor", "mar_bench_kv_concat"]
     b = _bench_lib.load_bench_library()
     for n in names:
         assert hasattr(ctypes.CDLL(str(_bench_lib._PATH)), n)
@@ -64,6 +64,15 @@ def test_bench_library_exports_and_rejections():
     assert g(P, P, P, P, P, P, P, 272, 2, 2, 320, 48, 272, 64, 7, None) == E_DTYPE
     assert g(P, P, P, P, P, P, P, 272, 2, 2, 320, 48, 272, 12, 1, None) == E_UNSUP    # 24-byte rows
     assert g(P, P, P, P, P, P, P, 100, 2, 2, 320, 48, 272, 64, 1, None) == E_SHAPE
+    d = b.mar_bench_dense_floor
+    # q, k, v, out, mode, B, H, N, D, dtype, stream
+    assert d(None, P, P, P, 1, 2, 2, 320, 64, 1, None) == E_NULL
+    assert d(P, P, P, P, 1, 2, 2, 320, 64, 0, None) == E_UNSUP    # fp32
+    assert d(P, P, P, P, 1, 0, 2, 320, 64, 1, None) == E_SHAPE
+    assert d(P, P, P, P, 1, 2, 2, 64, 64, 1, None) == E_UNSUP     # one wave's worth of tokens
+    assert d(P, P, P, P, 1, 2, 2, 320, 32, 1, None) == E_UNSUP    # head dim
+    assert d(P, P, P, P, 3, 2, 2, 320, 64, 1, None) == E_RANGE    # no such mode
+    assert d(P, P, P, BAD, 2, 2, 2, 320, 64, 1, None) == E_RANGE
 
 
 def test_status_strings(lib):

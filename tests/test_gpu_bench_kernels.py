@@ -69,3 +69,23 @@ def test_pattern_kernel_writes_only_its_rows(bench):
     # every 16-byte piece of the output rows was written
     pieces = buf[:B * H * A * D].view(-1, 8)
     assert not (pieces == sentinel).all(dim=1).any()
+
+
+def test_dense_floor_modes(bench):
+    """The full-attention kernel's measurement modes: the arithmetic-only mode
+    stores nothing (no memory traffic), the memory-only mode writes every
+    output row; both leave everything past the output untouched."""
+    from mar_workloads import device_normal
+    B, H, N, D = 2, 3, 400, 64
+    q, k, v = (device_normal((B, H, N, D), 90 + i, DEV, torch.bfloat16) for i in range(3))
+    sentinel = -12345
+    buf = torch.full((B * H * N * D + 4096,), sentinel, dtype=torch.int16, device=DEV)
+    out = buf[:B * H * N * D].view(torch.bfloat16).view(B, H, N, D)
+    bench.mar_bench_dense_floor(q, k, v, out, bench.MAR_BENCH_FLOOR_ARITH)
+    torch.cuda.synchronize()
+    assert (buf == sentinel).all()
+    bench.mar_bench_dense_floor(q, k, v, out, bench.MAR_BENCH_FLOOR_MEMORY)
+    torch.cuda.synchronize()
+    assert (buf[B * H * N * D:] == sentinel).all()
+    pieces = buf[:B * H * N * D].view(-1, 8)
+    assert not (pieces == sentinel).all(dim=1).any()
