@@ -948,6 +948,14 @@ def main():
         prepared(("full_floor", l, mode), _bench_lib.mar_bench_dense_floor, Lq["k_cache"],
                  L["k_cache"], L["v_cache"], x["full_out"], mode, stream=stream)()
 
+    def refresh_floor(l, mode):
+        """The refresh-step layer on full_refresh's buffers in a measurement mode."""
+        x = X[0]
+        L, Ln, Lq = (x["layers"][(l + i * (n_ca // 3)) % n_ca] for i in range(3))
+        prepared(("refresh_floor", l, mode), _bench_lib.mar_bench_dense_floor, Lq["k_cache"],
+                 Ln["k_cache"], Ln["v_cache"], x["full_out"], mode, k_cache=L["k_cache"],
+                 v_cache=L["v_cache"], stream=stream)()
+
     def timed_kernels():
         """The same launches as one step, grouped by kernel so that one pair of HIP
         events brackets each group of back-to-back launches (an event pair around
@@ -971,6 +979,10 @@ def main():
                                          for l in range(n_ca)], n_ca)
         span("full_memory_only", lambda: [full_floor(l, _bench_lib.MAR_BENCH_FLOOR_MEMORY)
                                           for l in range(n_ca)], n_ca)
+        span("refresh_arith_only", lambda: [refresh_floor(l, _bench_lib.MAR_BENCH_FLOOR_ARITH)
+                                            for l in range(n_ca)], n_ca)
+        span("refresh_memory_only", lambda: [refresh_floor(l, _bench_lib.MAR_BENCH_FLOOR_MEMORY)
+                                             for l in range(n_ca)], n_ca)
         span("attn_pattern", lambda: [pattern(l, True) for l in range(n_ca)], n_ca)
         span("attn_pattern_reads", lambda: [pattern(l, False) for l in range(n_ca)], n_ca)
         span("layer2_separate", lambda: [layer2_separate(l, plan) for l in range(n_ca)], n_ca)
@@ -1152,7 +1164,11 @@ def main():
                         "per-chunk math); the layer cannot take less than the larger",
                 "arith_only_us": avg_us["full_arith_only"],
                 "memory_only_us": avg_us["full_memory_only"],
-                "memory_only_gbs": full_bytes / (avg_us["full_memory_only"] * 1e-6) / 1e9}},
+                "memory_only_gbs": full_bytes / (avg_us["full_memory_only"] * 1e-6) / 1e9,
+                "refresh_arith_only_us": avg_us["refresh_arith_only"],
+                "refresh_memory_only_us": avg_us["refresh_memory_only"],
+                "refresh_memory_only_gbs": (full_bytes + 2 * full_bytes // 4)
+                                           / (avg_us["refresh_memory_only"] * 1e-6) / 1e9}},
         "decode": None if args.no_decode else {
             "what": "one 64-step decode of the attention path (every layer's attention, cache "
                     "writes, top-K, CFG and gate; no projections or MLPs), with the cache "

@@ -27,7 +27,7 @@ def load_bench_library():
         lib.mar_bench_kv_concat.restype = I
         lib.mar_bench_kv_concat.argtypes = [V, V, V, V, V, V, V, I, I, I, I, I, I, I, I, V]
         lib.mar_bench_dense_floor.restype = I
-        lib.mar_bench_dense_floor.argtypes = [V, V, V, V, I, I, I, I, I, I, V]
+        lib.mar_bench_dense_floor.argtypes = [V, V, V, V, V, V, I, I, I, I, I, I, V]
         _blib = lib
     return _blib
 
@@ -54,15 +54,20 @@ MAR_BENCH_FLOOR_ARITH = 1
 MAR_BENCH_FLOOR_MEMORY = 2
 
 
-def mar_bench_dense_floor(q, k, v, out, mode, stream=None):
+def mar_bench_dense_floor(q, k, v, out, mode, k_cache=None, v_cache=None, stream=None):
     """The full-attention kernel's arithmetic alone (MAR_BENCH_FLOOR_ARITH) or
     its memory operations alone (MAR_BENCH_FLOOR_MEMORY) over q, k, v, out
-    [B,H,N,D] (see mar_bench.h)."""
+    [B,H,N,D]; with k_cache, v_cache [B,H,N,D] the refresh-step layer's (see
+    mar_bench.h)."""
     B, H, N, D = q.shape
     for name, t in (("k", k), ("v", v), ("out", out)):
         _dev(t, name, q.dtype, (B, H, N, D))
-    _call("mar_bench_dense_floor", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-          int(mode), B, H, N, D, _dtype_code(q), _stream(stream), lib=load_bench_library())
+    caches = []
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        caches.append(None if t is None else _dev(t, name, q.dtype, (B, H, N, D)))
+    _call("mar_bench_dense_floor", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), caches[0],
+          caches[1], _dev(out, "out"), int(mode), B, H, N, D, _dtype_code(q), _stream(stream),
+          lib=load_bench_library())
     return out
 
 

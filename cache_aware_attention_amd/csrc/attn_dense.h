@@ -284,9 +284,10 @@ static_assert(kDenseQ % kChunk == 0, "Q row blocks follow the chunks");
 // LAB (measurement builds only; the decoding path uses kLabNone): kLabArith
 // keeps every instruction but turns each global load into a range-checked
 // load past the buffer (zeros, no memory traffic) and drops the output and
-// lse stores -- the kernel's arithmetic, LDS traffic and barriers alone;
-// kLabMemory skips the per-chunk math -- its loads, LDS stores, barriers and
-// output stores alone.
+// lse stores (and, with UPDATE, the cache writes) -- the kernel's
+// arithmetic, LDS traffic and barriers alone; kLabMemory skips the per-chunk
+// math -- its loads, LDS stores, barriers, cache writes and output stores
+// alone.
 constexpr int kLabNone = 0, kLabArith = 1, kLabMemory = 2;
 
 template <bool UPDATE, bool SHARED, int LAB = kLabNone>
@@ -336,6 +337,7 @@ void attn_dense_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restr
     const uint32_t piece = 16 * (tid & 7);
     const int lofs = swz(lrow, tid & 7);
     auto put_rows = [&](int u, int c, const uint4& kk, const uint4& vv) __attribute__((always_inline)) {
+        if constexpr (LAB == kLabArith) return;  // no memory traffic
         // the cache rows of chunk c of unit u (a row past A is dropped)
         const int r = c * kChunk + lrow;
         const uint32_t off = r < A ? static_cast<uint32_t>(r) * (kD * 2) + piece : kOut;

@@ -213,25 +213,34 @@ extern "C" int mar_bench_kv_concat(void* k_cat, void* v_cat, const void* k_a, co
     return status_from_launch();
 }
 
-extern "C" int mar_bench_dense_floor(const void* q, const void* k, const void* v, void* out,
-                                     int mode, int B, int H, int N, int D, int dtype,
-                                     void* stream) {
+extern "C" int mar_bench_dense_floor(const void* q, const void* k, const void* v,
+                                     void* k_cache, void* v_cache, void* out, int mode, int B,
+                                     int H, int N, int D, int dtype, void* stream) {
     using namespace marca;
     if (!q || !k || !v || !out) return MAR_E_NULL;
+    if ((k_cache == nullptr) != (v_cache == nullptr)) return MAR_E_NULL;
+    const bool update = k_cache != nullptr;
     if (dtype != MAR_BF16) return MAR_E_UNSUPPORTED;
     if (B < 1 || H < 1 || N < 1) return MAR_E_SHAPE;
     if (D != kD || N <= 64 || N > 8192) return MAR_E_UNSUPPORTED;
     if (mode != MAR_BENCH_FLOOR_ARITH && mode != MAR_BENCH_FLOOR_MEMORY) return MAR_E_RANGE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MAR_E_RANGE;
+    if (update && (!aligned16(k_cache) || !aligned16(v_cache))) return MAR_E_RANGE;
     auto qq = static_cast<const uint16_t*>(q);
     auto kk = static_cast<const uint16_t*>(k);
     auto vv = static_cast<const uint16_t*>(v);
     auto o = static_cast<uint16_t*>(out);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    auto kc = static_cast<uint16_t*>(k_cache);
+    auto vc = static_cast<uint16_t*>(v_cache);
     const float scale_log2 = 0.125f * 1.4426950408889634f;
     if (mode == MAR_BENCH_FLOOR_ARITH)
-        return launch_dense_wg<false, kLabArith>(qq, kk, vv, nullptr, nullptr, o, nullptr, B, H, N,
-                                                 scale_log2, s);
-    return launch_dense_wg<false, kLabMemory>(qq, kk, vv, nullptr, nullptr, o, nullptr, B, H, N,
-                                              scale_log2, s);
+        return update ? launch_dense_wg<true, kLabArith>(qq, kk, vv, kc, vc, o, nullptr, B, H, N,
+                                                         scale_log2, s)
+                      : launch_dense_wg<false, kLabArith>(qq, kk, vv, nullptr, nullptr, o, nullptr,
+                                                          B, H, N, scale_log2, s);
+    return update ? launch_dense_wg<true, kLabMemory>(qq, kk, vv, kc, vc, o, nullptr, B, H, N,
+                                                      scale_log2, s)
+                  : launch_dense_wg<false, kLabMemory>(qq, kk, vv, nullptr, nullptr, o, nullptr, B,
+                                                       H, N, scale_log2, s);
 }

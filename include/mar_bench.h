@@ -54,21 +54,26 @@ int mar_bench_kv_concat(void* k_cat, void* v_cat, const void* k_a, const void* v
 /*
  * The two floors of the full-attention layer (mar_cache_attn_fwd with
  * A == N, Nc == 0, more than 64 tokens: [MARche] Key Design 3, layers 1-2
- * and every layer of a refresh step), measured with the decoding path's own
- * kernel in a measurement mode:
+ * and every layer of a refresh step) and, with k_cache and v_cache given, of
+ * the refresh-step layer (mar_cache_attn_fwd_update with no active list: the
+ * same attention, every row of k and v also written to k_cache, v_cache
+ * [B,H,N,D]), measured with the decoding path's own kernel in a measurement
+ * mode:
  *   MAR_BENCH_FLOOR_ARITH   its arithmetic, LDS traffic and barriers alone:
  *                           every global load reads past its buffer (zeros,
  *                           no memory traffic) and nothing is stored;
  *   MAR_BENCH_FLOOR_MEMORY  its memory operations alone: it reads q, k, v
  *                           [B,H,N,D] and writes out [B,H,N,D] (meaningless
- *                           values) exactly as the layer does, without the
- *                           per-chunk math.
+ *                           values) -- and the caches -- exactly as the layer
+ *                           does, without the per-chunk math.
+ * k_cache and v_cache are both NULL or both given (MAR_E_NULL otherwise).
  * Requires bf16 (MAR_E_UNSUPPORTED otherwise), D == 64, 64 < N <= 8192;
  * another mode is MAR_E_RANGE.
  */
 enum { MAR_BENCH_FLOOR_ARITH = 1, MAR_BENCH_FLOOR_MEMORY = 2 };
-int mar_bench_dense_floor(const void* q, const void* k, const void* v, void* out, int mode,
-                          int B, int H, int N, int D, int dtype, void* stream);
+int mar_bench_dense_floor(const void* q, const void* k, const void* v, void* k_cache,
+                          void* v_cache, void* out, int mode, int B, int H, int N, int D,
+                          int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -65,14 +65,16 @@ def test_bench_library_exports_and_rejections():
     assert g(P, P, P, P, P, P, P, 272, 2, 2, 320, 48, 272, 12, 1, None) == E_UNSUP    # 24-byte rows
     assert g(P, P, P, P, P, P, P, 100, 2, 2, 320, 48, 272, 64, 1, None) == E_SHAPE
     d = b.mar_bench_dense_floor
-    # q, k, v, out, mode, B, H, N, D, dtype, stream
-    assert d(None, P, P, P, 1, 2, 2, 320, 64, 1, None) == E_NULL
-    assert d(P, P, P, P, 1, 2, 2, 320, 64, 0, None) == E_UNSUP    # fp32
-    assert d(P, P, P, P, 1, 0, 2, 320, 64, 1, None) == E_SHAPE
-    assert d(P, P, P, P, 1, 2, 2, 64, 64, 1, None) == E_UNSUP     # one wave's worth of tokens
-    assert d(P, P, P, P, 1, 2, 2, 320, 32, 1, None) == E_UNSUP    # head dim
-    assert d(P, P, P, P, 3, 2, 2, 320, 64, 1, None) == E_RANGE    # no such mode
-    assert d(P, P, P, BAD, 2, 2, 2, 320, 64, 1, None) == E_RANGE
+    # q, k, v, kc, vc, out, mode, B, H, N, D, dtype, stream
+    assert d(None, P, P, None, None, P, 1, 2, 2, 320, 64, 1, None) == E_NULL
+    assert d(P, P, P, P, None, P, 1, 2, 2, 320, 64, 1, None) == E_NULL      # one cache only
+    assert d(P, P, P, None, None, P, 1, 2, 2, 320, 64, 0, None) == E_UNSUP  # fp32
+    assert d(P, P, P, None, None, P, 1, 0, 2, 320, 64, 1, None) == E_SHAPE
+    assert d(P, P, P, None, None, P, 1, 2, 2, 64, 64, 1, None) == E_UNSUP   # one wave's tokens
+    assert d(P, P, P, None, None, P, 1, 2, 2, 320, 32, 1, None) == E_UNSUP  # head dim
+    assert d(P, P, P, None, None, P, 3, 2, 2, 320, 64, 1, None) == E_RANGE  # no such mode
+    assert d(P, P, P, None, None, BAD, 2, 2, 2, 320, 64, 1, None) == E_RANGE
+    assert d(P, P, P, BAD, P, P, 2, 2, 2, 320, 64, 1, None) == E_RANGE
 
 
 def test_status_strings(lib):

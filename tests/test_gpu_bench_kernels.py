@@ -89,3 +89,21 @@ def test_dense_floor_modes(bench):
     assert (buf[B * H * N * D:] == sentinel).all()
     pieces = buf[:B * H * N * D].view(-1, 8)
     assert not (pieces == sentinel).all(dim=1).any()
+
+
+def test_refresh_floor_modes(bench):
+    """The refresh-step layer's measurement modes: the arithmetic-only mode
+    writes neither the output nor the caches; the memory-only mode rewrites
+    every cache row with the fresh K/V, as the layer does."""
+    from mar_workloads import device_normal
+    B, H, N, D = 2, 3, 400, 64
+    q, k, v = (device_normal((B, H, N, D), 95 + i, DEV, torch.bfloat16) for i in range(3))
+    kc = torch.full((B, H, N, D), 5.0, dtype=torch.bfloat16, device=DEV)
+    vc = torch.full_like(kc, 5.0)
+    out = torch.full_like(kc, 7.0)
+    bench.mar_bench_dense_floor(q, k, v, out, bench.MAR_BENCH_FLOOR_ARITH, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    assert (kc == 5.0).all() and (vc == 5.0).all() and (out == 7.0).all()
+    bench.mar_bench_dense_floor(q, k, v, out, bench.MAR_BENCH_FLOOR_MEMORY, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k) and torch.equal(vc, v)
