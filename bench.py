@@ -413,6 +413,12 @@ def other_configs(marca, dev, stream):
             entry["full_attn_tflops"] = flops / f_us / 1e6
             entry["full_attn_roofline"] = roofline_for(flops, 4 * cfg.B * cfg.H * cfg.N * cfg.D * 2,
                                                        f_us * 1e-6)
+            # the same kernel's floors at this length (mar_bench_dense_floor)
+            from cache_aware_attention_amd import _bench_lib
+            for key, mode in (("full_attn_arith_only_us", _bench_lib.MAR_BENCH_FLOOR_ARITH),
+                              ("full_attn_memory_only_us", _bench_lib.MAR_BENCH_FLOOR_MEMORY)):
+                entry[key] = timed(lambda L, mode=mode: _bench_lib.mar_bench_dense_floor(
+                    qof[id(L)], L["k_cache"], L["v_cache"], full, mode))
             # refresh step: each layer's caches take the rows of the layer two
             # away as fresh K/V; the queries come from the layer four away
             nxt = {id(L): (layers[(i + 2) % len(layers)], layers[(i + 4) % len(layers)])
