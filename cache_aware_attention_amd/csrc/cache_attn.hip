@@ -28,11 +28,11 @@
 //    counts); the same MFMA tiles, with the softmax reference kept in scaled
 //    units and the query tiles in pairs.  Its 4 x 80-query form without
 //    cached rows serves layer 2's pass that also yields the refresh scores.
-//  * attn_dense_kernel (bf16, A > 64, no cached rows: the full-attention
+//  * attn_dense_kernel (attn_dense.h, with the per-chunk tile math it shares
+//    with attn_wg_kernel; bf16, A > 64, no cached rows: the full-attention
 //    layers and a refresh step's layers): persistent workgroups of 4 waves x
-//    80 queries with the same per-chunk math, whose chunk stream runs on from
-//    one (unit, query block) item to the next together with the next item's
-//    queries.
+//    80 queries, whose chunk stream runs on from one (unit, query block) item
+//    to the next together with the next item's queries.
 //  * attn_f32_mfma_kernel (fp32, A >= 16): one wave per unit and query group,
 //    S^T and O^T on v_mfma_f32_16x16x4_f32 with every operand loaded from
 //    memory straight into the layout the products take (no LDS tile).
