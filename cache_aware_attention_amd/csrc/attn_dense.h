@@ -97,8 +97,9 @@ struct WgTiles {
 // 8 rows).  kFull: every key row of the chunk
 // exists; kFirst: chunk 0, which sets the references.  CACHED: rows is the
 // chunk's row mask (bit k: row 32c + k exists); otherwise the rows at or past
-// A are missing (only a partial last chunk has any).
-template <int NQT, bool CACHED, bool kFull, bool kFirst>
+// A are missing (only a partial last chunk has any).  NT: the tiles computed,
+// the first NT of the wave's NQT (a wave with fewer queries skips the rest).
+template <int NQT, bool CACHED, bool kFull, bool kFirst, int NT = NQT>
 __device__ __forceinline__ void wg_chunk(WgTiles<NQT>& st, const unsigned char* kt,
                                          const unsigned char* vt, const int (&kofs)[2],
                                          const int (&vofs)[4], int c, int A, uint32_t rows,
@@ -211,12 +212,13 @@ __device__ __forceinline__ void wg_chunk(WgTiles<NQT>& st, const unsigned char* 
     // not wait for the maximum; the block that ends at a pair's test
     // then also holds the previous pair's conversions and P V MFMAs and
     // this pair's score MFMAs, which issue among the exponentials.
-    // Every tile is computed, also past nq (those rows repeat the last
-    // query and are never stored): a per-pair test would end the basic
-    // block early.
+    // Every one of the NT tiles is computed, also past nq (those rows repeat
+    // the last query and are never stored): a per-pair test would end the
+    // basic block early.
+    static_assert(NT >= 1 && NT <= NQT, "tiles computed");
 #pragma unroll
-    for (int qt = 0; qt < NQT; qt += 2) {
-        if (qt + 1 < NQT) {
+    for (int qt = 0; qt < NT; qt += 2) {
+        if (qt + 1 < NT) {
             float x0[8], x1[8], p0[8], p1[8];
             scores(qt, x0);
             scores(qt + 1, x1);

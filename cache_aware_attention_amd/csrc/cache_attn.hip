@@ -1168,8 +1168,24 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
         Ncn = min(max(c_len[u / H], 0), Nc);
         if (qb * W * kQ >= An) return;  // no queries in this block (uniform, before any barrier)
     }
-    const int q0 = (qb * W + w) * kQ;
-    const int nq = min(An - q0, kQ);  // <= 0: the wave loads and waits, computes nothing
+    // This wave's queries: nt 16-query tiles from q0.  CACHED: the block's
+    // tiles are spread evenly over its waves, one more for `extra` of them,
+    // a choice that rotates with the workgroup so no SIMD always takes the
+    // larger share (a ragged count of ~170 then keeps all four waves busy
+    // with three tiles or two, instead of three waves with four and one
+    // idle).  Otherwise kQ queries per wave.
+    int q0 = (qb * W + w) * kQ, nt = NQT;
+    if constexpr (CACHED) {
+        const int qbase = qb * W * kQ;
+        const int tiles = (min(An - qbase, W * kQ) + 15) / 16;  // An > qbase here
+        const int base = tiles / W, extra = tiles % W;
+        const int rot = static_cast<int>(blockIdx.x % W);
+        int t0 = 0;
+        for (int v = 0; v < w; ++v) t0 += base + ((v + rot) % W < extra ? 1 : 0);
+        nt = base + ((w + rot) % W < extra ? 1 : 0);
+        q0 = qbase + 16 * t0;
+    }
+    const int nq = min(An - q0, 16 * nt);  // <= 0: the wave loads and waits, computes nothing
     const size_t ub = static_cast<size_t>(u) * A * kD;
     // CACHED: the active rows fill chunks [0, na) (the last one padded), the
     // cached rows start on the next chunk: row A0 + j is cached entry j.
@@ -1274,11 +1290,13 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     // (set from the first chunk: active rows, the first of which exists).
     st.reset();
 
-    auto compute = [&](int c, int buf, uint32_t rows, auto full_tag, auto first_tag) __attribute__((always_inline)) {
+    // NT: the tiles the wave computes (its whole chunk loop is instantiated
+    // per tile count, so each copy keeps the registers of one).
+    auto compute = [&](int c, int buf, uint32_t rows, auto full_tag, auto first_tag, auto nt_tag) __attribute__((always_inline)) {
         const unsigned char* kt = SCORES ? kall + c * kWgTile : lds + buf * 2 * kWgTile;
         const unsigned char* vt = lds + buf * 2 * kWgTile + kWgTile;
-        wg_chunk<NQT, CACHED, decltype(full_tag)::value, decltype(first_tag)::value>(
-            st, kt, vt, kofs, vofs, c, A, rows, scale_log2, g);
+        wg_chunk<NQT, CACHED, decltype(full_tag)::value, decltype(first_tag)::value,
+                 decltype(nt_tag)::value>(st, kt, vt, kofs, vofs, c, A, rows, scale_log2, g);
     };
 
     // Chunk c sits in LDS buffer c % 2.  Each step requests chunk c + 1 into
@@ -1344,10 +1362,10 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     }
     put(0, 0, sk, sv);
     __syncthreads();
-    auto step = [&](int c, auto buf_tag, auto full_tag, auto first_tag, uint32_t rows = ~0u) __attribute__((always_inline)) {
+    auto step = [&](int c, auto buf_tag, auto full_tag, auto first_tag, auto nt_tag, uint32_t rows = ~0u) __attribute__((always_inline)) {
         constexpr int BI = decltype(buf_tag)::value;
         load(c + 1, sk, sv);  // past the last chunk: out-of-range offsets, no traffic
-        if (nq > 0) compute(c, BI, rows, full_tag, first_tag);
+        if (nq > 0) compute(c, BI, rows, full_tag, first_tag, nt_tag);
         put(BI ^ 1, c + 1, sk, sv);
         __syncthreads();
     };
@@ -1355,39 +1373,53 @@ void attn_wg_kernel(const uint16_t* __restrict__ q_a, const uint16_t* __restrict
     using B1 = std::integral_constant<int, 1>;
     using T1 = std::true_type;
     using F0 = std::false_type;
+    using NA = std::integral_constant<int, NQT>;
     if constexpr (!CACHED) {
         // The chunks without rows past A, in pairs (constant buffer indices),
         // then the partial last chunk if A is not a multiple of 32: only that
         // one carries the masking.
         const int nfull = A / kChunk;  // >= 2 (A > 64)
-        step(0, B0{}, T1{}, T1{});
+        step(0, B0{}, T1{}, T1{}, NA{});
         int c = 1;
         for (; c + 1 < nfull; c += 2) {
-            step(c, B1{}, T1{}, F0{});
-            step(c + 1, B0{}, T1{}, F0{});
+            step(c, B1{}, T1{}, F0{}, NA{});
+            step(c + 1, B0{}, T1{}, F0{}, NA{});
         }
-        if (c < nfull) step(c++, B1{}, T1{}, F0{});
+        if (c < nfull) step(c++, B1{}, T1{}, F0{}, NA{});
         if (c < nchunks) {
             if (c & 1)
-                step(c, B1{}, F0{}, F0{});
+                step(c, B1{}, F0{}, F0{}, NA{});
             else
-                step(c, B0{}, F0{}, F0{});
+                step(c, B0{}, F0{}, F0{}, NA{});
         }
     } else {
         // Every chunk's scores start from its row mask (uniform).  Chunk 0
         // sets the references; it holds active rows only, all of them unless
-        // a sequence's count is below 32.
-        auto step_any = [&](int c, auto buf_tag) __attribute__((always_inline)) {
-            step(c, buf_tag, T1{}, F0{},
-                 __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cflag_s[c])));
+        // a sequence's count is below 32.  The loop runs at the wave's tile
+        // count (every copy passes the same barriers).
+        auto chunks = [&](auto nt_tag) __attribute__((always_inline)) {
+            auto step_any = [&](int c, auto buf_tag) __attribute__((always_inline)) {
+                step(c, buf_tag, T1{}, F0{}, nt_tag,
+                     __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cflag_s[c])));
+            };
+            step(0, B0{}, T1{}, T1{}, nt_tag,
+                 __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cflag_s[0])));
+            int c = 1;
+            for (; c + 1 < nchunks; c += 2) {
+                step_any(c, B1{});
+                step_any(c + 1, B0{});
+            }
+            if (c < nchunks) step_any(c, B1{});
         };
-        step(0, B0{}, T1{}, T1{}, __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cflag_s[0])));
-        int c = 1;
-        for (; c + 1 < nchunks; c += 2) {
-            step_any(c, B1{});
-            step_any(c + 1, B0{});
-        }
-        if (c < nchunks) step_any(c, B1{});
+        static_assert(NQT == 4, "cached workgroup tiles");
+        if (nt >= 4)
+            chunks(std::integral_constant<int, 4>{});
+        else if (nt == 3)
+            chunks(std::integral_constant<int, 3>{});
+        else if (nt == 2)
+            chunks(std::integral_constant<int, 2>{});
+        else  // one tile, or none (nq <= 0: the wave only loads)
+            chunks(std::integral_constant<int, 1>{});
     }
 
     if constexpr (SCORES) {
