@@ -120,18 +120,22 @@ __device__ __forceinline__ void wg_chunk(WgTiles<NQT>& st, const unsigned char* 
     }
     const int r0 = c * kChunk;
     // CACHED: the score MFMAs start from 0 for a key row that exists and
-    // from -inf for one that does not (rows: the chunk's row mask), so
-    // every chunk takes the same path.  Otherwise (no cached rows) only
-    // the partial last chunk masks, here: the lane's key rows 16t + 4g + i
-    // that exist, at bits 16t + i.
+    // from -inf for one that does not (rows: the chunk's row mask, uniform),
+    // so every chunk takes the same path; the per-row values are formed only
+    // for a chunk with a missing row (a partial last chunk or skipped list
+    // entries).  Otherwise (no cached rows) only the partial last chunk
+    // masks, here: the lane's key rows 16t + 4g + i that exist, at bits
+    // 16t + i.
     f32x4_t bias[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
     if constexpr (CACHED) {
-        const uint32_t have = rows >> (4 * g);
+        if (__builtin_expect(rows != ~0u, 0)) {
+            const uint32_t have = rows >> (4 * g);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                bias[t][i] = ((have >> (16 * t + i)) & 1u) ? 0.f : -INFINITY;
+                for (int i = 0; i < 4; ++i)
+                    bias[t][i] = ((have >> (16 * t + i)) & 1u) ? 0.f : -INFINITY;
+        }
     }
     uint32_t have = 0;
     if constexpr (!kFull && !CACHED) {
