@@ -401,6 +401,14 @@ def other_configs(marca, dev, stream):
                  "attn_frac_hbm": gbs / PEAK_HBM_GBS, "attn_bytes_per_call": nbytes,
                  "attn_tflops": 4 * cfg.B * cfg.H * cfg.A * (cfg.A + cfg.Nc) * cfg.D / us / 1e6}
         if name == "highres":
+            # the same kernel's floors (mar_bench_cached_floor): its
+            # arithmetic alone and its memory operations alone
+            from cache_aware_attention_amd import _bench_lib
+            for key, mode in (("attn_arith_only_us", _bench_lib.MAR_BENCH_FLOOR_ARITH),
+                              ("attn_memory_only_us", _bench_lib.MAR_BENCH_FLOOR_MEMORY)):
+                entry[key] = timed(lambda L, mode=mode: _bench_lib.mar_bench_cached_floor(
+                    L["q_a"], L["k_a"], L["v_a"], L["k_cache"], L["v_cache"], L["cached"],
+                    L["out"], mode, Nc=cfg.Nc))
             full = torch.empty_like(layers[0]["k_cache"])
             flops = 4 * cfg.B * cfg.H * cfg.N * cfg.N * cfg.D
             # the queries: the K of the layer three away (no tensor is read
@@ -414,7 +422,6 @@ def other_configs(marca, dev, stream):
             entry["full_attn_roofline"] = roofline_for(flops, 4 * cfg.B * cfg.H * cfg.N * cfg.D * 2,
                                                        f_us * 1e-6)
             # the same kernel's floors at this length (mar_bench_dense_floor)
-            from cache_aware_attention_amd import _bench_lib
             for key, mode in (("full_attn_arith_only_us", _bench_lib.MAR_BENCH_FLOOR_ARITH),
                               ("full_attn_memory_only_us", _bench_lib.MAR_BENCH_FLOOR_MEMORY)):
                 entry[key] = timed(lambda L, mode=mode: _bench_lib.mar_bench_dense_floor(
@@ -430,14 +437,67 @@ def other_configs(marca, dev, stream):
             g_bytes = 2 * cfg.B * cfg.N * 1024 * 2 + cfg.B * cfg.N * 9
             entry["gate_us_per_call"] = g_us
             entry["gate_gbs"] = g_bytes / (g_us * 1e-6) / 1e9
+            gl = {k: torch.empty((cfg.B, cfg.N), dtype=t, device=dev) for k, t in
+                  (("cos", torch.float32), ("reuse", torch.uint8), ("cidx", torch.int32),
+                   ("ridx", torch.int32))}
+            gl["clen"], gl["rlen"] = (torch.empty((cfg.B,), dtype=torch.int32, device=dev)
+                                      for _ in range(2))
+            marca.mar_cos_gate(gx, gy, 0.95, cos_out=gl["cos"], reuse_mask=gl["reuse"],
+                               compute_idx=gl["cidx"], compute_len=gl["clen"],
+                               reuse_idx=gl["ridx"], reuse_len=gl["rlen"])
+            torch.cuda.synchronize()
             del gx, gy
             entry["refresh_us_per_call"] = timed(
                 lambda L: marca.mar_cache_attn_fwd_update(
                     nxt[id(L)][1]["k_cache"], nxt[id(L)][0]["k_cache"], nxt[id(L)][0]["v_cache"],
                     L["k_cache"], L["v_cache"], None, None, Nc=0, out=full))
+            entry["gated_layer"] = gated_layer(marca, _bench_lib, cfg, layers, gl, dev, timed)
         res[name] = entry
         del layers
         torch.cuda.empty_cache()
+    return res
+
+
+def gated_layer(marca, bench_lib, cfg, layers, gl, dev, timed):
+    """One gated layer of the high-res decode on each of the layers' caches:
+    each sequence's recomputed tokens (the gate's compute list for seeded
+    features at 84% reuse) attend over their fresh K/V and the cached K/V of
+    the reused tokens, whose cache rows they replace in the same pass
+    (mar_cache_attn_fwd_ragged_update), and the same kernel's floors."""
+    import torch
+
+    from mar_workloads import device_normal
+    a = gl["clen"].long()
+    cap = int(a.max())
+    B, H, N, D = cfg.B, cfg.H, cfg.N, cfg.D
+    x = {id(L): [device_normal((B, H, cap, D), 7700 + 3 * i + j, dev, torch.bfloat16)
+                 for j in range(3)] + [torch.empty((B, H, cap, D), dtype=torch.bfloat16, device=dev)]
+         for i, L in enumerate(layers)}
+    torch.cuda.synchronize()
+
+    def call(L, mode=None):
+        q, k, v, o = x[id(L)]
+        if mode is None:
+            marca.mar_cache_attn_fwd_ragged_update(q, k, v, L["k_cache"], L["v_cache"], gl["ridx"],
+                                                   gl["cidx"], gl["clen"], gl["rlen"], out=o)
+        else:
+            bench_lib.mar_bench_cached_floor(q, k, v, L["k_cache"], L["v_cache"], gl["ridx"], o,
+                                             mode, active_idx=gl["cidx"], a_len=gl["clen"],
+                                             c_len=gl["rlen"])
+
+    us = timed(call)
+    # fresh Q/K/V/out of the recomputed rows, the reused rows' cached K/V, the
+    # recomputed rows' cache writes, the reuse list: B*H*(4a + 2N)*D*2 + B*N*4
+    nbytes = int((H * (4 * a + 2 * N) * D * 2).sum()) + B * N * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res = {"what": "mar_cache_attn_fwd_ragged_update at the high-res gated layers' counts; "
+                   "floors as for the full attention (mar_bench_cached_floor)",
+           "recomputed_mean": float(a.float().mean()), "recomputed_capacity": cap,
+           "us_per_call": us, "bytes_per_call": nbytes, "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+           "tflops": 4 * H * D * N * float(a.sum()) / us / 1e6,
+           "arith_only_us": timed(lambda L: call(L, bench_lib.MAR_BENCH_FLOOR_ARITH)),
+           "memory_only_us": timed(lambda L: call(L, bench_lib.MAR_BENCH_FLOOR_MEMORY))}
+    del x
     return res
 
 

@@ -22,7 +22,7 @@
 //    (no per-chunk math): the two floors that bound the full-attention layer.
 #include <type_traits>
 
-#include "attn_dense.h"
+#include "attn_cached.h"
 #include "device_util.h"
 #include "mar_bench.h"
 
@@ -243,4 +243,50 @@ extern "C" int mar_bench_dense_floor(const void* q, const void* k, const void* v
                                                       scale_log2, s)
                   : launch_dense_wg<false, kLabMemory>(qq, kk, vv, nullptr, nullptr, o, nullptr, B,
                                                        H, N, scale_log2, s);
+}
+
+extern "C" int mar_bench_cached_floor(const void* q_a, const void* k_a, const void* v_a,
+                                      void* k_cache, void* v_cache, const int32_t* cached_idx,
+                                      int ldc, const int32_t* active_idx, int ld_act,
+                                      const int32_t* a_len, const int32_t* c_len, void* out,
+                                      int mode, int B, int H, int N, int A, int Nc, int D,
+                                      int dtype, void* stream) {
+    using namespace marca;
+    if (!q_a || !k_a || !v_a || !k_cache || !v_cache || !cached_idx || !out) return MAR_E_NULL;
+    if ((a_len == nullptr) != (c_len == nullptr)) return MAR_E_NULL;
+    const bool ragged = a_len != nullptr;
+    const bool update = active_idx != nullptr;
+    if (ragged != update) return MAR_E_UNSUPPORTED;  // the two forms the decoding path runs
+    if (dtype != MAR_BF16) return MAR_E_UNSUPPORTED;
+    if (B < 1 || H < 1 || N < 1 || A < 1 || Nc < 1) return MAR_E_SHAPE;
+    // per-sequence counts: A and Nc are capacities, each at most N
+    if (ragged ? (A > N || Nc > N) : (static_cast<long long>(A) + Nc > N)) return MAR_E_SHAPE;
+    if (ldc < Nc || (update && ld_act < A)) return MAR_E_SHAPE;
+    if (D != kD || A <= 64 || N > 8192) return MAR_E_UNSUPPORTED;
+    if (cached_wg_lds(update, A, Nc) > kCachedWgMaxLds) return MAR_E_UNSUPPORTED;
+    if (mode != MAR_BENCH_FLOOR_ARITH && mode != MAR_BENCH_FLOOR_MEMORY) return MAR_E_RANGE;
+    if (!aligned16(q_a) || !aligned16(k_a) || !aligned16(v_a) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out))
+        return MAR_E_RANGE;
+    auto q = static_cast<const uint16_t*>(q_a);
+    auto k = static_cast<const uint16_t*>(k_a);
+    auto v = static_cast<const uint16_t*>(v_a);
+    auto kc = static_cast<const uint16_t*>(k_cache);
+    auto vc = static_cast<const uint16_t*>(v_cache);
+    auto o = static_cast<uint16_t*>(out);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale_log2 = 0.125f * 1.4426950408889634f;
+    auto go = [&](auto lab_tag) {
+        constexpr int kLab = decltype(lab_tag)::value;
+        return update ? launch_cached_wg<true, true, kLab>(q, k, v, kc, vc, cached_idx, ldc, o,
+                                                            nullptr, B, H, N, A, Nc, scale_log2,
+                                                            active_idx, ld_act, nullptr, a_len,
+                                                            c_len, s)
+                      : launch_cached_wg<false, false, kLab>(q, k, v, kc, vc, cached_idx, ldc, o,
+                                                              nullptr, B, H, N, A, Nc, scale_log2,
+                                                              nullptr, 0, nullptr, nullptr,
+                                                              nullptr, s);
+    };
+    return mode == MAR_BENCH_FLOOR_ARITH ? go(std::integral_constant<int, kLabArith>{})
+                                         : go(std::integral_constant<int, kLabMemory>{});
 }

@@ -75,6 +75,33 @@ int mar_bench_dense_floor(const void* q, const void* k, const void* v, void* k_c
                           void* v_cache, void* out, int mode, int B, int H, int N, int D,
                           int dtype, void* stream);
 
+/*
+ * The same two floors for the cache-aware layers whose active queries fill
+ * several waves ([MARche] Key Design 2, Eq. 1-2, at the high-res length; the
+ * [LazyMAR] notes page, token cache: each sequence's recomputed tokens),
+ * measured with the decoding path's workgroup kernel in the modes above:
+ *   - uniform counts, no update (active_idx, a_len, c_len all NULL): the
+ *     layer of mar_cache_attn_fwd with A active rows and Nc cached entries,
+ *     A + Nc <= N;
+ *   - per-sequence counts with the cache update (active_idx, a_len, c_len
+ *     all given): the layer of mar_cache_attn_fwd_ragged_update, with A and
+ *     Nc as capacities (each <= N) and ld_act >= A.
+ * Arguments as for those calls: q_a, k_a, v_a, out [B,H,A,D]; k_cache,
+ * v_cache [B,H,N,D]; cached_idx [B,ldc]; active_idx [B,ld_act]; a_len, c_len
+ * [B].  The arithmetic-only mode writes neither out nor the caches; the
+ * memory-only mode writes out (meaningless values) and, with the update,
+ * the caches as the layer does.  Requires bf16, D == 64, A > 64, Nc >= 1,
+ * N <= 8192 and the staged lists within the workgroup's LDS
+ * (MAR_E_UNSUPPORTED otherwise; a_len without c_len is MAR_E_NULL, and so
+ * is a missing pointer).  The other combinations of the optional lists are
+ * MAR_E_UNSUPPORTED; another mode is MAR_E_RANGE.
+ */
+int mar_bench_cached_floor(const void* q_a, const void* k_a, const void* v_a, void* k_cache,
+                           void* v_cache, const int32_t* cached_idx, int ldc,
+                           const int32_t* active_idx, int ld_act, const int32_t* a_len,
+                           const int32_t* c_len, void* out, int mode, int B, int H, int N, int A,
+                           int Nc, int D, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

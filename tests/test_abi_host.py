@@ -46,7 +46,8 @@ def test_bench_library_exports_and_rejections():
     declares and refuses bad arguments before any GPU work."""
     from cache_aware_attention_amd import _bench_lib
     names = declared_functions(os.path.join(ROOT, "include", "mar_bench.h"))
-    assert names == ["mar_bench_attn_pattern", "mar_bench_dense_floor", "mar_bench_kv_concat"]
+    assert names == ["mar_bench_attn_pattern", "mar_bench_cached_floor", "mar_bench_dense_floor",
+                     "mar_bench_kv_concat"]
     b = _bench_lib.load_bench_library()
     for n in names:
         assert hasattr(ctypes.CDLL(str(_bench_lib._PATH)), n)
@@ -75,6 +76,31 @@ def test_bench_library_exports_and_rejections():
     assert d(P, P, P, None, None, P, 3, 2, 2, 320, 64, 1, None) == E_RANGE  # no such mode
     assert d(P, P, P, None, None, BAD, 2, 2, 2, 320, 64, 1, None) == E_RANGE
     assert d(P, P, P, BAD, P, P, 2, 2, 2, 320, 64, 1, None) == E_RANGE
+    c = b.mar_bench_cached_floor
+    # q, ka, va, kc, vc, cidx, ldc, act, ld_act, a_len, c_len, out, mode, B, H, N, A, Nc, D,
+    # dtype, stream
+    assert c(P, P, P, P, P, None, 960, None, 0, None, None, P, 1, 2, 2, 1088, 128, 960, 64, 1,
+             None) == E_NULL
+    assert c(P, P, P, P, P, P, 1088, P, 200, P, None, P, 1, 2, 2, 1088, 200, 1088, 64, 1,
+             None) == E_NULL                                                     # a_len only
+    assert c(P, P, P, P, P, P, 960, P, 128, None, None, P, 1, 2, 2, 1088, 128, 960, 64, 1,
+             None) == E_UNSUP                                                    # uniform update
+    assert c(P, P, P, P, P, P, 960, None, 0, None, None, P, 1, 2, 2, 1088, 128, 960, 64, 0,
+             None) == E_UNSUP                                                    # fp32
+    assert c(P, P, P, P, P, P, 961, None, 0, None, None, P, 1, 2, 2, 1088, 128, 961, 64, 1,
+             None) == E_SHAPE                                                    # A+Nc > N
+    assert c(P, P, P, P, P, P, 1088, P, 200, P, P, P, 1, 2, 2, 1088, 200, 1089, 64, 1,
+             None) == E_SHAPE                                                    # Nc > N
+    assert c(P, P, P, P, P, P, 900, None, 0, None, None, P, 1, 2, 2, 1088, 128, 960, 64, 1,
+             None) == E_SHAPE                                                    # ldc < Nc
+    assert c(P, P, P, P, P, P, 1088, P, 100, P, P, P, 1, 2, 2, 1088, 200, 1088, 64, 1,
+             None) == E_SHAPE                                                    # ld_act < A
+    assert c(P, P, P, P, P, P, 960, None, 0, None, None, P, 1, 2, 2, 1088, 64, 960, 64, 1,
+             None) == E_UNSUP                                                    # one wave
+    assert c(P, P, P, P, P, P, 960, None, 0, None, None, P, 3, 2, 2, 1088, 128, 960, 64, 1,
+             None) == E_RANGE                                                    # no such mode
+    assert c(P, P, P, P, P, P, 960, None, 0, None, None, BAD, 2, 2, 2, 1088, 128, 960, 64, 1,
+             None) == E_RANGE
 
 
 def test_status_strings(lib):
