@@ -64,6 +64,15 @@ def fused_bytes(B, H, A, Nc, D, elem=2):
     return attn_bytes(B, H, A, Nc, D, elem) + 2 * B * H * A * D * elem
 
 
+def ragged_update_bytes(H, N, D, counts, elem=2):
+    """Algorithmic bytes of mar_cache_attn_fwd_ragged_update over all N tokens
+    of each sequence, a[b] = counts[b] of them recomputed: their fresh Q, K, V
+    read and out written (4 a rows), the reused tokens' cached K and V read
+    (2 (N - a) rows), the recomputed rows' K and V written into the caches
+    (2 a rows), per head; and each sequence's N-entry int32 reuse list."""
+    return sum(H * (4 * a + 2 * N) * D * elem for a in counts) + len(counts) * N * 4
+
+
 def headline_record(cfg, n_ca, steps, warmup, ms_per_step, achieved_gbs, traffic, cpu):
     """The required part of the one-line JSON record.  `value` is active-query
     tokens per second of the whole step: B x A queries in each of the n_ca
@@ -486,9 +495,7 @@ def gated_layer(marca, bench_lib, cfg, layers, gl, dev, timed):
                                              c_len=gl["rlen"])
 
     us = timed(call)
-    # fresh Q/K/V/out of the recomputed rows, the reused rows' cached K/V, the
-    # recomputed rows' cache writes, the reuse list: B*H*(4a + 2N)*D*2 + B*N*4
-    nbytes = int((H * (4 * a + 2 * N) * D * 2).sum()) + B * N * 4
+    nbytes = ragged_update_bytes(H, N, D, a.tolist())
     gbs = nbytes / (us * 1e-6) / 1e9
     res = {"what": "mar_cache_attn_fwd_ragged_update at the high-res gated layers' counts; "
                    "floors as for the full attention (mar_bench_cached_floor)",

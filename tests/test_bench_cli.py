@@ -40,6 +40,16 @@ def test_attention_algorithmic_bytes():
     assert b.fused_bytes(128, 16, 48, 272, 64) == 218243072
 
 
+def test_ragged_update_algorithmic_bytes():
+    b = load_bench()
+    # one sequence, one head, 10 tokens, 3 recomputed: 4 x 3 fresh rows (Q, K,
+    # V read, out written), 2 x 7 reused rows read, 2 x 3 rows written into
+    # the caches, the 10-entry list
+    assert b.ragged_update_bytes(1, 10, 64, [3]) == (12 + 14 + 6) * 128 + 40
+    # per sequence, summed: counts 0 and 10 (nothing and everything recomputed)
+    assert b.ragged_update_bytes(2, 10, 64, [0, 10]) == 2 * (20 + 60) * 128 + 2 * 40
+
+
 def test_traffic_only_for_the_measured_source(tmp_path):
     b = load_bench()
     src = tmp_path / "kernel.hip"
