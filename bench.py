@@ -409,6 +409,13 @@ def other_configs(marca, dev, stream):
                  "cached": cfg.Nc, "attn_us_per_call": us, "attn_gbs": gbs,
                  "attn_frac_hbm": gbs / PEAK_HBM_GBS, "attn_bytes_per_call": nbytes,
                  "attn_tflops": 4 * cfg.B * cfg.H * cfg.A * (cfg.A + cfg.Nc) * cfg.D / us / 1e6}
+        if name in ("mar_b", "mar_h"):
+            # the floor of the call's access pattern (mar_bench_attn_pattern:
+            # the same loads and stores, no arithmetic)
+            from cache_aware_attention_amd import _bench_lib
+            entry["attn_pattern_us"] = timed(lambda L: _bench_lib.mar_bench_attn_pattern(
+                L["q_a"], L["k_a"], L["v_a"], L["k_cache"], L["v_cache"], L["cached"], cfg.Nc,
+                L["out"]))
         if name == "highres":
             # the same kernel's floors (mar_bench_cached_floor): its
             # arithmetic alone and its memory operations alone
